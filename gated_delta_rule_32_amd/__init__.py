@@ -1,0 +1,304 @@
+"""Python binding of libkda, the MI355X (gfx950) KDA training recurrence.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libkda.so, called through its C ABI (include/libkda.h).  PyTorch
+supplies device memory and the current stream.
+
+Low-level functions carry the C names (kda_fwd, kda_bwd, kda_fwd_ctx_bytes,
+kda_bwd_workspace_bytes, kda_plan_query, kda_status_string, kda_last_error,
+kda_version).  The paired training API mirrors the FlashInfer pages
+"flashinfer.kda_training.recurrent_kda_training_forward" and
+"flashinfer.kda_training" (recurrent_kda_training_backward).
+
+The library must be built first (``python -m gated_delta_rule_32_amd.build_lib``);
+importing this package without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+HEAD_DIM = 128
+SCALE = 1.0 / math.sqrt(128.0)
+
+KDA_OK = 0
+KDA_ERR_HIP = 12
+ROUTE_AUTO, ROUTE_CHUNK, ROUTE_ROWSPLIT = 0, 1, 2
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libkda.so not found at {LIB_PATH}; build it with "
+        "`python -m gated_delta_rule_32_amd.build_lib` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class KdaProblem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hqk", ctypes.c_int32),
+        ("Hv", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+        ("scale", ctypes.c_float), ("lower_bound", ctypes.c_float),
+        ("route", ctypes.c_int32), ("checkpoint_every", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.POINTER(KdaProblem)
+_vp = ctypes.c_void_p
+_lib.kda_version.restype = ctypes.c_int
+_lib.kda_status_string.restype = ctypes.c_char_p
+_lib.kda_status_string.argtypes = [ctypes.c_int]
+_lib.kda_last_error.restype = ctypes.c_char_p
+_lib.kda_fwd_ctx_bytes.restype = ctypes.c_int
+_lib.kda_fwd_ctx_bytes.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t)]
+_lib.kda_bwd_workspace_bytes.restype = ctypes.c_int
+_lib.kda_bwd_workspace_bytes.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t)]
+_lib.kda_plan_query.restype = ctypes.c_int
+_lib.kda_plan_query.argtypes = [_P, ctypes.POINTER(ctypes.c_int32),
+                                ctypes.POINTER(ctypes.c_int64), _vp, ctypes.c_int64]
+_lib.kda_fwd.restype = ctypes.c_int
+_lib.kda_fwd.argtypes = [_P] + [_vp] * 10 + [_vp, ctypes.c_size_t, _vp]
+_lib.kda_bwd.restype = ctypes.c_int
+_lib.kda_bwd.argtypes = ([_P] + [_vp] * 8 + [_vp, ctypes.c_size_t] + [_vp] * 2 + [_vp] * 8
+                         + [_vp, ctypes.c_size_t, _vp])
+
+EXPORTED = ("kda_version", "kda_status_string", "kda_last_error", "kda_fwd_ctx_bytes",
+            "kda_bwd_workspace_bytes", "kda_plan_query", "kda_fwd", "kda_bwd")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{kda_status_string(status)}: {msg}")
+        self.status = status
+
+
+class KdaValueError(ValueError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{kda_status_string(status)}: {msg}")
+        self.status = status
+
+
+def kda_version() -> int:
+    return int(_lib.kda_version())
+
+
+def kda_status_string(status: int) -> str:
+    return _lib.kda_status_string(int(status)).decode()
+
+
+def kda_last_error() -> str:
+    return _lib.kda_last_error().decode()
+
+
+def _check(status: int):
+    if status == KDA_OK:
+        return
+    msg = kda_last_error()
+    if status == KDA_ERR_HIP:
+        raise KdaError(status, msg)
+    raise KdaValueError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def make_problem(B: int, T: int, Hqk: int, Hv: int, N: int,
+                 cu_seqlens: Optional[torch.Tensor] = None,
+                 cu_seqlens_cpu: Optional[torch.Tensor] = None,
+                 scale: Optional[float] = None, lower_bound: float = -5.0,
+                 route: int = ROUTE_AUTO, checkpoint_every: int = 0) -> KdaProblem:
+    p = KdaProblem()
+    p.B, p.T, p.Hqk, p.Hv, p.N = int(B), int(T), int(Hqk), int(Hv), int(N)
+    p.cu_seqlens = _ptr(cu_seqlens)
+    p.cu_seqlens_host = _ptr(cu_seqlens_cpu)
+    p.scale = 0.0 if scale is None else float(scale)
+    p.lower_bound = float(lower_bound)
+    p.route = int(route)
+    p.checkpoint_every = int(checkpoint_every)
+    return p
+
+
+def kda_fwd_ctx_bytes(p: KdaProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.kda_fwd_ctx_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
+def kda_bwd_workspace_bytes(p: KdaProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.kda_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
+def kda_plan_query(p: KdaProblem, with_order: bool = False):
+    """(route, num_tasks, order or None): host planning only."""
+    route = ctypes.c_int32(0)
+    nt = ctypes.c_int64(0)
+    _check(_lib.kda_plan_query(ctypes.byref(p), ctypes.byref(route), ctypes.byref(nt), None, 0))
+    order = None
+    if with_order:
+        buf = (ctypes.c_int32 * int(nt.value))()
+        _check(_lib.kda_plan_query(ctypes.byref(p), None, None, ctypes.cast(buf, _vp),
+                                   int(nt.value)))
+        order = list(buf)
+    return int(route.value), int(nt.value), order
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def kda_fwd(p: KdaProblem, q, k, v, g, beta, A_log, dt_bias, initial_state, o, final_state,
+            ctx: Optional[torch.Tensor], stream: Optional[int] = None) -> None:
+    """C kda_fwd on torch tensors (no shape checks beyond the library's)."""
+    if stream is None:
+        stream = _stream_handle(q.device)
+    ctx_bytes = 0 if ctx is None else ctx.numel() * ctx.element_size()
+    _check(_lib.kda_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                        _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(o),
+                        _ptr(final_state), _ptr(ctx), ctx_bytes, stream))
+
+
+def kda_bwd(p: KdaProblem, q, k, v, g, beta, A_log, dt_bias, initial_state, ctx, d_o,
+            dfinal_state, dq, dk, dv, dg, dbeta, dA_log, ddt_bias, dinitial_state,
+            workspace: torch.Tensor, stream: Optional[int] = None) -> None:
+    """C kda_bwd on torch tensors."""
+    if stream is None:
+        stream = _stream_handle(q.device)
+    _check(_lib.kda_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                        _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(ctx),
+                        ctx.numel() * ctx.element_size(), _ptr(d_o), _ptr(dfinal_state),
+                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dA_log),
+                        _ptr(ddt_bias), _ptr(dinitial_state), _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), stream))
+
+
+# ---------------------------------------------------------------------------
+# paired training API
+# ---------------------------------------------------------------------------
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(name, t, dtype, shape, device):
+    _require(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _require(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _require(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+    _require(t.device == device, f"{name} must be on {device}, got {t.device}")
+
+
+@dataclass
+class RecurrentKDATrainingContext:
+    """What the forward saved for the backward: the problem, the state tape
+    (a byte tensor on the device) and the inputs with their versions."""
+    problem: KdaProblem
+    ctx: torch.Tensor
+    inputs: tuple
+    versions: tuple
+    cu_seqlens: Optional[torch.Tensor]
+    cu_seqlens_cpu: Optional[torch.Tensor]
+    stream: int
+
+
+def _problem_from(q, v, cu_seqlens, cu_seqlens_cpu, scale, lower_bound, route, checkpoint_every):
+    _require(q.dim() == 4 and v.dim() == 4, "q and v must be [B, T, H, 128]")
+    B, T, Hqk, Dq = q.shape
+    Hv = v.shape[2]
+    _require(Dq == HEAD_DIM and v.shape[3] == HEAD_DIM, "head dimensions must be 128")
+    if cu_seqlens is not None:
+        _require(cu_seqlens_cpu is not None, "packed calls need cu_seqlens_cpu")
+        _require(cu_seqlens.dtype == torch.int64 and cu_seqlens_cpu.dtype == torch.int64,
+                 "cu_seqlens must be int64")
+        _require(cu_seqlens_cpu.device.type == "cpu" and cu_seqlens_cpu.is_contiguous(),
+                 "cu_seqlens_cpu must be a contiguous CPU tensor")
+        _require(cu_seqlens.is_contiguous() and cu_seqlens.device == q.device,
+                 "cu_seqlens must be contiguous on the device of q")
+        N = cu_seqlens.numel() - 1
+    else:
+        _require(cu_seqlens_cpu is None, "cu_seqlens_cpu must be omitted for fixed layout")
+        N = B
+    return make_problem(B, T, Hqk, Hv, N, cu_seqlens, cu_seqlens_cpu, scale, lower_bound,
+                        route, checkpoint_every)
+
+
+def recurrent_kda_training_forward(q, k, v, g, beta, A_log, dt_bias, initial_state,
+                                   cu_seqlens=None, scale=None, lower_bound=-5.0, out=None,
+                                   final_state_out=None, context_out=None, *,
+                                   cu_seqlens_cpu=None, route: int = ROUTE_AUTO,
+                                   checkpoint_every: int = 0, save_context: bool = True):
+    """Forward of the KDA training recurrence: returns (o, final_state, ctx)."""
+    dev = q.device
+    p = _problem_from(q, v, cu_seqlens, cu_seqlens_cpu, scale, lower_bound, route,
+                      checkpoint_every)
+    B, T, Hqk, Hv, N = p.B, p.T, p.Hqk, p.Hv, p.N
+    bf = torch.bfloat16
+    _check_tensor("q", q, bf, (B, T, Hqk, 128), dev)
+    _check_tensor("k", k, bf, (B, T, Hqk, 128), dev)
+    _check_tensor("v", v, bf, (B, T, Hv, 128), dev)
+    _check_tensor("g", g, bf, (B, T, Hv, 128), dev)
+    _check_tensor("beta", beta, bf, (B, T, Hv), dev)
+    _check_tensor("A_log", A_log, torch.float32, (Hv,), dev)
+    _check_tensor("dt_bias", dt_bias, torch.float32, (Hv, 128), dev)
+    _check_tensor("initial_state", initial_state, torch.float32, (N, Hv, 128, 128), dev)
+    o = out if out is not None else torch.empty((B, T, Hv, 128), dtype=bf, device=dev)
+    _check_tensor("out", o, bf, (B, T, Hv, 128), dev)
+    fs = final_state_out if final_state_out is not None else torch.empty_like(initial_state)
+    _check_tensor("final_state_out", fs, torch.float32, (N, Hv, 128, 128), dev)
+    ctx_t = None
+    if save_context:
+        need = kda_fwd_ctx_bytes(p)
+        if context_out is not None:
+            _require(context_out.ctx.numel() >= need and context_out.ctx.device == dev,
+                     "context_out does not fit this call")
+            _require(context_out.stream == _stream_handle(dev),
+                     "a context is reused only on the stream that created it")
+            ctx_t = context_out.ctx
+        else:
+            ctx_t = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = _stream_handle(dev)
+    kda_fwd(p, q, k, v, g, beta, A_log, dt_bias, initial_state, o, fs, ctx_t, stream)
+    ctx = None
+    if save_context:
+        inputs = (q, k, v, g, beta, A_log, dt_bias, initial_state)
+        ctx = RecurrentKDATrainingContext(p, ctx_t, inputs, tuple(t._version for t in inputs),
+                                          cu_seqlens, cu_seqlens_cpu, stream)
+    return o, fs, ctx
+
+
+def recurrent_kda_training_backward(context: RecurrentKDATrainingContext, do, dfinal_state,
+                                    out: Optional[Sequence[torch.Tensor]] = None,
+                                    workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv, dg, dbeta, dA_log, ddt_bias, dinitial_state)."""
+    _require(context is not None, "context is required")
+    inputs = context.inputs
+    now = tuple(t._version for t in inputs)
+    _require(now == context.versions, "an input changed after the forward (tensor version)")
+    q, k, v, g, beta, A_log, dt_bias, s0 = inputs
+    p = context.problem
+    dev = q.device
+    _check_tensor("do", do, torch.bfloat16, tuple(v.shape), dev)
+    _check_tensor("dfinal_state", dfinal_state, torch.float32, tuple(s0.shape), dev)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g),
+               torch.empty_like(beta), torch.empty_like(A_log), torch.empty_like(dt_bias),
+               torch.empty_like(s0))
+    _require(len(out) == 8, "out must hold eight tensors")
+    for name, t, ref in zip(("dq", "dk", "dv", "dg", "dbeta", "dA_log", "ddt_bias",
+                             "dinitial_state"), out, inputs):
+        _check_tensor(name, t, ref.dtype, tuple(ref.shape), dev)
+    need = kda_bwd_workspace_bytes(p)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    kda_bwd(p, q, k, v, g, beta, A_log, dt_bias, s0, context.ctx, do, dfinal_state, *out,
+            workspace, _stream_handle(dev))
+    return tuple(out)

@@ -1,0 +1,526 @@
+// libkda C ABI: argument checks, host planning, context records, launches.
+//
+// Contract sources (FlashInfer KDA pages): "flashinfer.kda_training.recurrent_
+// kda_training_forward" (parameters), "flashinfer.kda_training" (paragraphs
+// 1-4: overlap rule, context reuse on its own device and stream, head and
+// layout rules, non-empty sequences, fixed scale and lower bound),
+// "flashinfer.kda.recurrent_kda" (parameter cu_seqlens: host-side
+// longest-first order cached per unchanged offsets).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/libkda.h"
+#include "kda_kernels.h"
+
+namespace {
+
+constexpr int D = 128;  // head dimension
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+kda_status hip_fail(hipError_t e, const char* what) {
+    return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kStateElems = (int64_t)D * D;
+constexpr int kDefaultCk = 256;
+constexpr int kChunk = 16;
+
+// A validated problem.
+struct Prob {
+    int B, T, Hqk, Hv, N, G;
+    bool packed;
+    int route;      // resolved: 1 chunk, 2 rowsplit
+    int ck;         // tape interval
+    float scale;
+    std::vector<int64_t> len;    // per sequence
+    std::vector<int64_t> start;  // flattened token offset per sequence
+    int64_t tokens;              // B * T
+    int64_t num_tasks;
+    int64_t total_ck;            // stored checkpoints (sum ceil(L/ck) - 1)
+    int64_t total_chunks;        // sum ceil(L/16)
+    int64_t total_segs;          // sum ceil(L/ck)
+};
+
+int auto_route(const Prob& p) {
+    // The chunked MFMA kernel needs enough (sequence, head) tasks to occupy
+    // the 256 compute units; with few tasks the row-split kernel, which
+    // spreads each task's rows over 8 workgroups, keeps more of the chip busy.
+    return (p.num_tasks >= 64) ? 1 : 2;
+}
+
+kda_status validate(const kda_problem* p, Prob& out) {
+    if (p == nullptr) return fail(KDA_ERR_NULL_ARG, "problem is NULL");
+    if (p->B < 1 || p->T < 1 || p->Hqk < 1 || p->Hv < 1 || p->N < 1)
+        return fail(KDA_ERR_SHAPE, "B, T, Hqk, Hv and N must be >= 1 (got %d %d %d %d %d)",
+                    p->B, p->T, p->Hqk, p->Hv, p->N);
+    if (p->Hv % p->Hqk != 0)
+        return fail(KDA_ERR_GROUPING, "Hv (%d) must be a multiple of Hqk (%d)", p->Hv, p->Hqk);
+    if ((int64_t)p->N * p->Hv > (int64_t)INT32_MAX / 2)
+        return fail(KDA_ERR_SHAPE, "too many (sequence, head) tasks");
+    const bool packed = p->cu_seqlens != nullptr || p->cu_seqlens_host != nullptr;
+    if (packed && (p->cu_seqlens == nullptr || p->cu_seqlens_host == nullptr))
+        return fail(KDA_ERR_NULL_ARG, "packed layout needs both cu_seqlens and cu_seqlens_host");
+    const float want_scale = 1.0f / std::sqrt(128.0f);
+    float scale = p->scale;
+    if (scale == 0.0f) scale = want_scale;
+    if (std::fabs(scale - want_scale) > 1e-6f * want_scale)
+        return fail(KDA_ERR_SCALE, "scale must be 1/sqrt(128) (got %g)", (double)p->scale);
+    if (p->lower_bound != -5.0f)
+        return fail(KDA_ERR_LOWER_BOUND, "lower_bound must be -5 (got %g)", (double)p->lower_bound);
+    if (p->route < 0 || p->route > 2) return fail(KDA_ERR_ROUTE, "unknown route %d", p->route);
+    int ck = p->checkpoint_every == 0 ? kDefaultCk : p->checkpoint_every;
+    if (ck <= 0 || ck % kChunk != 0)
+        return fail(KDA_ERR_ROUTE, "checkpoint_every must be a positive multiple of 16 (got %d)",
+                    p->checkpoint_every);
+
+    out = Prob{};
+    out.B = p->B; out.T = p->T; out.Hqk = p->Hqk; out.Hv = p->Hv; out.N = p->N;
+    out.G = p->Hv / p->Hqk;
+    out.packed = packed;
+    out.ck = ck;
+    out.scale = want_scale;
+    out.tokens = (int64_t)p->B * p->T;
+    if (packed) {
+        if (p->B != 1) return fail(KDA_ERR_SHAPE, "packed layout needs B == 1 (got %d)", p->B);
+        const int64_t* cu = p->cu_seqlens_host;
+        if (cu[0] != 0) return fail(KDA_ERR_SEQLENS, "cu_seqlens must start at 0");
+        for (int n = 0; n < p->N; ++n) {
+            if (cu[n + 1] <= cu[n])
+                return fail(KDA_ERR_SEQLENS, "sequence %d is empty or offsets decrease", n);
+        }
+        if (cu[p->N] != p->T)
+            return fail(KDA_ERR_SEQLENS, "cu_seqlens must end at T=%d (got %lld)", p->T,
+                        (long long)cu[p->N]);
+        out.len.resize(p->N);
+        out.start.resize(p->N);
+        for (int n = 0; n < p->N; ++n) {
+            out.start[n] = cu[n];
+            out.len[n] = cu[n + 1] - cu[n];
+        }
+    } else {
+        if (p->N != p->B)
+            return fail(KDA_ERR_SHAPE, "fixed layout needs N == B (got N=%d, B=%d)", p->N, p->B);
+        out.len.assign(p->N, p->T);
+        out.start.resize(p->N);
+        for (int n = 0; n < p->N; ++n) out.start[n] = (int64_t)n * p->T;
+    }
+    out.num_tasks = (int64_t)p->N * p->Hv;
+    out.total_ck = out.total_chunks = out.total_segs = 0;
+    for (int64_t L : out.len) {
+        out.total_ck += (L + ck - 1) / ck - 1;
+        out.total_segs += (L + ck - 1) / ck;
+        out.total_chunks += (L + kChunk - 1) / kChunk;
+    }
+    out.route = p->route == 0 ? auto_route(out) : p->route;
+    return KDA_OK;
+}
+
+// Longest sequence first; ties keep sequence order.  Within a sequence the
+// value heads follow each other, so heads sharing a q/k head are adjacent.
+std::vector<int32_t> lpt_order(const Prob& p) {
+    std::vector<int> seqs(p.N);
+    for (int n = 0; n < p.N; ++n) seqs[n] = n;
+    std::stable_sort(seqs.begin(), seqs.end(),
+                     [&](int a, int b) { return p.len[a] > p.len[b]; });
+    std::vector<int32_t> order;
+    order.reserve((size_t)p.num_tasks);
+    for (int n : seqs)
+        for (int h = 0; h < p.Hv; ++h) order.push_back(n * p.Hv + h);
+    return order;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// Device schedule cache
+// ---------------------------------------------------------------------------
+struct PlanEntry {
+    void* dev = nullptr;
+    void* host = nullptr;
+    hipEvent_t ready = nullptr;
+    size_t off_task = 0, off_start = 0, off_len = 0, off_tape = 0, off_chunk = 0, off_seg = 0;
+    size_t bytes = 0;
+};
+
+std::mutex g_mu;
+std::map<std::vector<int64_t>, std::unique_ptr<PlanEntry>> g_plans;
+constexpr size_t kMaxPlans = 4096;
+
+std::vector<int64_t> plan_key(const Prob& p, int dev) {
+    std::vector<int64_t> key = {dev, p.Hv, p.ck, p.packed ? 1 : 0, p.T, p.N};
+    key.insert(key.end(), p.len.begin(), p.len.end());
+    return key;
+}
+
+kda_status get_plan(const Prob& p, hipStream_t stream, int dev, const PlanEntry** out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto key = plan_key(p, dev);
+    auto it = g_plans.find(key);
+    if (it != g_plans.end()) {
+        hipError_t e = hipStreamWaitEvent(stream, it->second->ready, 0);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        *out = it->second.get();
+        return KDA_OK;
+    }
+    if (g_plans.size() >= kMaxPlans)
+        return fail(KDA_ERR_HIP, "schedule cache full (%zu distinct length sets)", g_plans.size());
+    auto ent = std::make_unique<PlanEntry>();
+    size_t off = 0;
+    ent->off_task = off;  off = align256(off + sizeof(int32_t) * (size_t)p.num_tasks);
+    ent->off_start = off; off = align256(off + sizeof(int64_t) * (size_t)p.N);
+    ent->off_len = off;   off = align256(off + sizeof(int32_t) * (size_t)p.N);
+    ent->off_tape = off;  off = align256(off + sizeof(int64_t) * (size_t)(p.N + 1));
+    ent->off_chunk = off; off = align256(off + sizeof(int64_t) * (size_t)(p.N + 1));
+    ent->off_seg = off;   off = align256(off + sizeof(int32_t) * 2 * (size_t)p.total_segs);
+    ent->bytes = off;
+    hipError_t e = hipHostMalloc(&ent->host, ent->bytes, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(schedule)");
+    char* h = (char*)ent->host;
+    std::vector<int32_t> order = lpt_order(p);
+    std::memcpy(h + ent->off_task, order.data(), sizeof(int32_t) * order.size());
+    int64_t* st = (int64_t*)(h + ent->off_start);
+    int32_t* ln = (int32_t*)(h + ent->off_len);
+    int64_t* to = (int64_t*)(h + ent->off_tape);
+    int64_t* co = (int64_t*)(h + ent->off_chunk);
+    int32_t* sg = (int32_t*)(h + ent->off_seg);
+    to[0] = 0;
+    co[0] = 0;
+    int64_t si = 0;
+    // segments in longest-first order of their sequences
+    std::vector<int> seqs(p.N);
+    for (int n = 0; n < p.N; ++n) {
+        seqs[n] = n;
+        st[n] = p.start[n];
+        ln[n] = (int32_t)p.len[n];
+        to[n + 1] = to[n] + (p.len[n] + p.ck - 1) / p.ck - 1;
+        co[n + 1] = co[n] + (p.len[n] + kChunk - 1) / kChunk;
+    }
+    std::stable_sort(seqs.begin(), seqs.end(), [&](int a, int b) { return p.len[a] > p.len[b]; });
+    for (int n : seqs) {
+        const int64_t nseg = (p.len[n] + p.ck - 1) / p.ck;
+        for (int64_t j = 0; j < nseg; ++j) {
+            sg[2 * si] = n;
+            sg[2 * si + 1] = (int32_t)j;
+            ++si;
+        }
+    }
+    e = hipMalloc(&ent->dev, ent->bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(schedule)");
+    e = hipMemcpyAsync(ent->dev, ent->host, ent->bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(schedule)");
+    e = hipEventCreateWithFlags(&ent->ready, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    e = hipEventRecord(ent->ready, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    *out = ent.get();
+    g_plans.emplace(std::move(key), std::move(ent));
+    return KDA_OK;
+}
+
+kda::DevPlan dev_plan(const PlanEntry* e) {
+    const char* d = (const char*)e->dev;
+    kda::DevPlan p;
+    p.task = (const int32_t*)(d + e->off_task);
+    p.seq_start = (const int64_t*)(d + e->off_start);
+    p.seq_len = (const int32_t*)(d + e->off_len);
+    p.tape_off = (const int64_t*)(d + e->off_tape);
+    p.chunk_off = (const int64_t*)(d + e->off_chunk);
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// Context records (what kda_bwd checks)
+// ---------------------------------------------------------------------------
+struct CtxRecord {
+    std::vector<int64_t> key;   // plan key (device, Hv, ck, layout, lengths)
+    int B, T, Hqk, Hv, N, route;
+    const void* ptrs[8];
+    hipStream_t stream;
+    size_t ctx_bytes;
+};
+std::map<const void*, CtxRecord> g_ctx;
+
+size_t tape_bytes(const Prob& p) {
+    return (size_t)p.total_ck * (size_t)p.Hv * (size_t)kStateElems * sizeof(float);
+}
+size_t ctx_bytes_for(const Prob& p) { return 256 + tape_bytes(p); }
+
+struct Span {
+    const void* p;
+    size_t n;
+    const char* name;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+    if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+    const char* a0 = (const char*)a.p;
+    const char* b0 = (const char*)b.p;
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+kda_status check_overlap(const std::vector<Span>& outs, const std::vector<Span>& ins) {
+    for (size_t i = 0; i < outs.size(); ++i) {
+        for (size_t j = i + 1; j < outs.size(); ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(KDA_ERR_OVERLAP, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+        for (const Span& s : ins)
+            if (overlaps(outs[i], s))
+                return fail(KDA_ERR_OVERLAP, "output %s overlaps %s", outs[i].name, s.name);
+    }
+    return KDA_OK;
+}
+
+std::vector<Span> input_spans(const Prob& p, const void* q, const void* k, const void* v,
+                              const void* g, const void* beta, const float* A_log,
+                              const float* dt_bias, const float* s0, const int64_t* cu) {
+    const size_t tq = (size_t)p.tokens * p.Hqk * D * 2;
+    const size_t tv = (size_t)p.tokens * p.Hv * D * 2;
+    const size_t st = (size_t)p.N * p.Hv * kStateElems * 4;
+    return {{q, tq, "q"}, {k, tq, "k"}, {v, tv, "v"}, {g, tv, "g"},
+            {beta, (size_t)p.tokens * p.Hv * 2, "beta"}, {A_log, (size_t)p.Hv * 4, "A_log"},
+            {dt_bias, (size_t)p.Hv * D * 4, "dt_bias"}, {s0, st, "initial_state"},
+            {cu, cu ? (size_t)(p.N + 1) * 8 : 0, "cu_seqlens"}};
+}
+
+kda::FwdArgs make_fwd_args(const Prob& p, const PlanEntry* plan, const void* q, const void* k,
+                           const void* v, const void* g, const void* beta, const float* A_log,
+                           const float* dt_bias, const float* s0) {
+    kda::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+    a.A_log = A_log; a.dt_bias = dt_bias; a.s0 = s0;
+    a.plan = dev_plan(plan);
+    a.Hqk = p.Hqk; a.Hv = p.Hv; a.G = p.G;
+    a.num_tasks = (int)p.num_tasks;
+    a.ck_every = p.ck;
+    a.scale = p.scale;
+    a.seg_mode = -1;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return KDA_VERSION; }
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL_ARG: return "null argument";
+        case KDA_ERR_SHAPE: return "bad shape";
+        case KDA_ERR_GROUPING: return "Hv is not a multiple of Hqk";
+        case KDA_ERR_SEQLENS: return "bad cu_seqlens";
+        case KDA_ERR_SCALE: return "scale must be 1/sqrt(128)";
+        case KDA_ERR_LOWER_BOUND: return "lower_bound must be -5";
+        case KDA_ERR_OVERLAP: return "output overlaps another buffer";
+        case KDA_ERR_CTX_SIZE: return "context too small";
+        case KDA_ERR_CTX_MISMATCH: return "context does not match this call";
+        case KDA_ERR_WORKSPACE_SIZE: return "workspace too small";
+        case KDA_ERR_ROUTE: return "bad route or checkpoint interval";
+        case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+kda_status kda_fwd_ctx_bytes(const kda_problem* pp, size_t* bytes) {
+    Prob p;
+    kda_status s = validate(pp, p);
+    if (s != KDA_OK) return s;
+    if (bytes == nullptr) return fail(KDA_ERR_NULL_ARG, "bytes is NULL");
+    *bytes = ctx_bytes_for(p);
+    return KDA_OK;
+}
+
+static size_t ws_layout(const Prob& p, size_t* off_states, size_t* off_dqk, size_t* off_par) {
+    size_t off = 0;
+    *off_states = off;
+    off = align256(off + (size_t)p.total_chunks * p.Hv * kStateElems * sizeof(float));
+    *off_dqk = off;
+    if (p.G > 1) off = align256(off + (size_t)p.tokens * p.Hv * 2 * D * sizeof(float));
+    *off_par = off;
+    off = align256(off + (size_t)p.num_tasks * 2 * D * sizeof(float));
+    return off;
+}
+
+kda_status kda_bwd_workspace_bytes(const kda_problem* pp, size_t* bytes) {
+    Prob p;
+    kda_status s = validate(pp, p);
+    if (s != KDA_OK) return s;
+    if (bytes == nullptr) return fail(KDA_ERR_NULL_ARG, "bytes is NULL");
+    size_t a, b, c;
+    *bytes = ws_layout(p, &a, &b, &c);
+    return KDA_OK;
+}
+
+kda_status kda_plan_query(const kda_problem* pp, int32_t* route, int64_t* num_tasks,
+                          int32_t* order, int64_t cap) {
+    Prob p;
+    kda_status s = validate(pp, p);
+    if (s != KDA_OK) return s;
+    if (route) *route = p.route;
+    if (num_tasks) *num_tasks = p.num_tasks;
+    if (order != nullptr && cap > 0) {
+        std::vector<int32_t> o = lpt_order(p);
+        std::memcpy(order, o.data(), sizeof(int32_t) * (size_t)std::min<int64_t>(cap, (int64_t)o.size()));
+    }
+    return KDA_OK;
+}
+
+kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const void* v,
+                   const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                   const float* initial_state, void* o, float* final_state, void* ctx,
+                   size_t ctx_bytes, void* stream_) {
+    Prob p;
+    kda_status s = validate(pp, p);
+    if (s != KDA_OK) return s;
+    if (!q || !k || !v || !g || !beta || !A_log || !dt_bias || !initial_state || !o || !final_state)
+        return fail(KDA_ERR_NULL_ARG, "a tensor argument of kda_fwd is NULL");
+    if (ctx != nullptr && ctx_bytes < ctx_bytes_for(p))
+        return fail(KDA_ERR_CTX_SIZE, "context has %zu bytes, needs %zu", ctx_bytes, ctx_bytes_for(p));
+    if (ctx == nullptr && ctx_bytes != 0)
+        return fail(KDA_ERR_NULL_ARG, "ctx is NULL but ctx_bytes is %zu", ctx_bytes);
+    std::vector<Span> ins = input_spans(p, q, k, v, g, beta, A_log, dt_bias, initial_state,
+                                        pp->cu_seqlens);
+    const size_t tv = (size_t)p.tokens * p.Hv * D * 2;
+    const size_t st = (size_t)p.N * p.Hv * kStateElems * 4;
+    std::vector<Span> outs = {{o, tv, "o"}, {final_state, st, "final_state"},
+                              {ctx, ctx ? ctx_bytes : 0, "ctx"}};
+    s = check_overlap(outs, ins);
+    if (s != KDA_OK) return s;
+
+    hipStream_t stream = (hipStream_t)stream_;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    const PlanEntry* plan = nullptr;
+    s = get_plan(p, stream, dev, &plan);
+    if (s != KDA_OK) return s;
+
+    kda::FwdArgs a = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, initial_state);
+    a.o = o;
+    a.s_final = final_state;
+    a.tape = ctx ? (float*)((char*)ctx + 256) : nullptr;
+    e = (p.route == 1) ? kda::launch_fwd_chunk(a, stream) : kda::launch_fwd_rowsplit(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    if (ctx != nullptr) {
+        CtxRecord r;
+        r.key = plan_key(p, dev);
+        r.B = p.B; r.T = p.T; r.Hqk = p.Hqk; r.Hv = p.Hv; r.N = p.N; r.route = p.route;
+        const void* ptrs[8] = {q, k, v, g, beta, A_log, dt_bias, initial_state};
+        std::memcpy(r.ptrs, ptrs, sizeof(ptrs));
+        r.stream = stream;
+        r.ctx_bytes = ctx_bytes;
+        std::lock_guard<std::mutex> lock(g_mu);
+        g_ctx[ctx] = r;
+    }
+    return KDA_OK;
+}
+
+kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const void* v,
+                   const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                   const float* initial_state, const void* ctx, size_t ctx_bytes,
+                   const void* d_o, const float* dfinal_state, void* dq, void* dk, void* dv,
+                   void* dg, void* dbeta, float* dA_log, float* ddt_bias, float* dinitial_state,
+                   void* workspace, size_t workspace_bytes, void* stream_) {
+    Prob p;
+    kda_status s = validate(pp, p);
+    if (s != KDA_OK) return s;
+    if (!q || !k || !v || !g || !beta || !A_log || !dt_bias || !initial_state || !ctx || !d_o ||
+        !dfinal_state || !dq || !dk || !dv || !dg || !dbeta || !dA_log || !ddt_bias ||
+        !dinitial_state || !workspace)
+        return fail(KDA_ERR_NULL_ARG, "a tensor argument of kda_bwd is NULL");
+    if (ctx_bytes < ctx_bytes_for(p))
+        return fail(KDA_ERR_CTX_SIZE, "context has %zu bytes, needs %zu", ctx_bytes, ctx_bytes_for(p));
+    size_t off_states, off_dqk, off_par;
+    const size_t need = ws_layout(p, &off_states, &off_dqk, &off_par);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE_SIZE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    hipStream_t stream = (hipStream_t)stream_;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_ctx.find(ctx);
+        if (it == g_ctx.end())
+            return fail(KDA_ERR_CTX_MISMATCH, "context was not filled by kda_fwd");
+        const CtxRecord& r = it->second;
+        const void* ptrs[8] = {q, k, v, g, beta, A_log, dt_bias, initial_state};
+        if (r.key != plan_key(p, dev) || r.B != p.B || r.T != p.T || r.Hqk != p.Hqk ||
+            r.Hv != p.Hv || r.N != p.N)
+            return fail(KDA_ERR_CTX_MISMATCH, "context was made for another shape or device");
+        if (std::memcmp(r.ptrs, ptrs, sizeof(ptrs)) != 0)
+            return fail(KDA_ERR_CTX_MISMATCH, "inputs differ from the forward that made the context");
+        if (r.stream != stream)
+            return fail(KDA_ERR_CTX_MISMATCH, "context is used on another stream than its forward's");
+    }
+    std::vector<Span> ins = input_spans(p, q, k, v, g, beta, A_log, dt_bias, initial_state,
+                                        pp->cu_seqlens);
+    const size_t tq = (size_t)p.tokens * p.Hqk * D * 2;
+    const size_t tv = (size_t)p.tokens * p.Hv * D * 2;
+    const size_t st = (size_t)p.N * p.Hv * kStateElems * 4;
+    ins.push_back({ctx, ctx_bytes, "ctx"});
+    ins.push_back({d_o, tv, "do"});
+    ins.push_back({dfinal_state, st, "dfinal_state"});
+    std::vector<Span> outs = {{dq, tq, "dq"}, {dk, tq, "dk"}, {dv, tv, "dv"}, {dg, tv, "dg"},
+                              {dbeta, (size_t)p.tokens * p.Hv * 2, "dbeta"},
+                              {dA_log, (size_t)p.Hv * 4, "dA_log"},
+                              {ddt_bias, (size_t)p.Hv * D * 4, "ddt_bias"},
+                              {dinitial_state, st, "dinitial_state"},
+                              {workspace, workspace_bytes, "workspace"}};
+    s = check_overlap(outs, ins);
+    if (s != KDA_OK) return s;
+
+    const PlanEntry* plan = nullptr;
+    s = get_plan(p, stream, dev, &plan);
+    if (s != KDA_OK) return s;
+
+    kda::BwdArgs b{};
+    b.f = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, initial_state);
+    b.f.tape = (float*)((char*)ctx + 256);
+    char* ws = (char*)workspace;
+    b.f.chunk_states = (float*)(ws + off_states);
+    b.d_o = d_o; b.dfinal = dfinal_state;
+    b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg; b.dbeta = dbeta;
+    b.dA_log = dA_log; b.ddt_bias = ddt_bias; b.dinit = dinitial_state;
+    b.chunk_states = (const float*)(ws + off_states);
+    b.dqk_part = p.G > 1 ? (float*)(ws + off_dqk) : nullptr;
+    b.dparam_part = (float*)(ws + off_par);
+    b.total_tokens = p.tokens;
+
+    // segment list sits after the chunk offsets in the schedule
+    kda::FwdArgs rb = b.f;
+    rb.plan.task = (const int32_t*)((const char*)plan->dev + plan->off_seg);
+    e = kda::launch_state_rebuild(rb, p.total_segs * p.Hv, stream);
+    if (e != hipSuccess) return hip_fail(e, "state rebuild launch");
+    e = kda::launch_bwd_chunk(b, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    e = kda::launch_bwd_reduce(b, p.N, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward reduction launch");
+    return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Device helpers shared by the libkda kernels (gfx950 / CDNA4).
+//
+// BF16 values live in memory as __bf16.  Conversions FP32 -> BF16 round to
+// nearest even (gfx950 has a hardware instruction for the packed form).
+//
+// MFMA fragment convention used throughout.  A "frag" is a 16x16 FP32 tile
+// in the accumulator layout of the 16x16 MFMA instructions: lane l = 16*gq + n
+// holds rows 4*gq + i (i = 0..3) of column n.  A 16x16xK MFMA multiplies the
+// A-register element i of lane (gq, m) with the B-register element i of lane
+// (gq, n) and sums over gq and i; so the product X*Y is formed from
+//   * the frag of X^T (lane (gq, m) holds X[m][4gq+i])   as the A operand, and
+//   * the frag of Y   (lane (gq, n) holds Y[4gq+i][n])   as the B operand,
+// and the contraction index may be renumbered freely as long as both operands
+// agree.  The 16x16x32 form takes two such frags per operand (contraction
+// blocks 2j and 2j+1) concatenated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = 128;          // head dimension (K = V = 128)
+constexpr int CH = 16;          // chunk length in tokens
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+__device__ __forceinline__ bf16 f2bf(float x) { return (bf16)x; }
+
+// exp(x) through the hardware base-2 exponential.
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+
+// 1/sqrt(x) (hardware approximation, ~1 ulp).
+__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
+
+// sigmoid(x) = 1 / (1 + exp(-x)), saturating cleanly at both ends.
+__device__ __forceinline__ float sigmoidf_(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x));
+}
+
+// --- MFMA wrappers -------------------------------------------------------
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
+    bf16x4 r;
+    r[0] = (bf16)x[0]; r[1] = (bf16)x[1]; r[2] = (bf16)x[2]; r[3] = (bf16)x[3];
+    return r;
+}
+// FP32 x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): the pair carries
+// about 16 significant bits, so hi*hi' + hi*lo' + lo*hi' reproduces an FP32
+// product to ~2^-16 relative.
+__device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bf16 h = (bf16)x[i];
+        hi[i] = h;
+        lo[i] = (bf16)(x[i] - (float)h);
+    }
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Sum over groups of `W` consecutive lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+}  // namespace kda

@@ -1,0 +1,64 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Device-side schedule built on the host from the sequence lengths.  Task i
+// (0 <= i < num_tasks, longest sequence first) is (n, h) = (task[i] / Hv,
+// task[i] % Hv).  Sequence n occupies flattened tokens [seq_start[n],
+// seq_start[n] + seq_len[n]) of the [B*T] token axis.  tape_off[n] counts the
+// stored checkpoints of the sequences before n (ceil(L/C_ck) - 1 each) and
+// chunk_off[n] the 16-token chunks (ceil(L/16) each).
+struct DevPlan {
+    const int32_t* task;
+    const int64_t* seq_start;
+    const int32_t* seq_len;
+    const int64_t* tape_off;
+    const int64_t* chunk_off;
+};
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* A_log;
+    const float* dt_bias;
+    const float* s0;        // [N][Hv][128][128]
+    void* o;
+    float* s_final;         // [N][Hv][128][128]; may be null (state rebuild)
+    float* tape;            // [ck][Hv][128][128]; may be null
+    float* chunk_states;    // [chunks][Hv][128][128] state at every chunk start; may be null
+    DevPlan plan;
+    int Hqk, Hv, G;
+    int num_tasks;
+    int ck_every;           // tape interval (tokens), multiple of 16
+    float scale;
+    // state rebuild mode: process only the tokens of tape segment `seg`
+    // (0 = from the initial state); -1 = whole sequence
+    int seg_mode;
+};
+
+struct BwdArgs {
+    FwdArgs f;              // inputs and plan (o, s_final unused)
+    const void* d_o;
+    const float* dfinal;
+    void* dq; void* dk; void* dv; void* dg; void* dbeta;
+    float* dA_log; float* ddt_bias; float* dinit;
+    const float* chunk_states;  // rebuilt chunk-start states
+    float* dqk_part;        // [tokens][Hv][2][128] FP32 partial dq,dk when G > 1; else null
+    float* dparam_part;     // [tasks][2][128]: per-task ddt_bias and dA_log partial sums
+    int64_t total_tokens;
+};
+
+hipError_t launch_fwd_rowsplit(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s);
+hipError_t launch_state_rebuild(const FwdArgs& a, int64_t num_items, hipStream_t s);
+hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_reduce(const BwdArgs& a, int N, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,162 @@
+/*
+ * libkda — recurrent Kimi Delta Attention (KDA) training recurrence on AMD
+ * Instinct MI355X (gfx950).  C ABI.
+ *
+ * What is computed (FlashInfer page "flashinfer.kda_backward.recurrent_kda_
+ * backward", description; page "flashinfer.kda_training.recurrent_kda_training_
+ * forward", parameter list).  For every sequence n and value head h, with the
+ * q/k head hq = h / (Hv/Hqk), a 128x128 FP32 value-first state S[v][k] starts
+ * at initial_state[n][h] and, token by token,
+ *
+ *     qn = q / sqrt(|q|^2 + 1e-6),   kn = k / sqrt(|k|^2 + 1e-6)
+ *     alpha = exp(-5 * sigmoid(exp(A_log[h]) * (g + dt_bias[h][:])))   (per key)
+ *     beta  = sigmoid(beta_logit)
+ *     S <- S diag(alpha);   S <- S + beta (v - S kn) kn^T;   o = S qn / sqrt(128)
+ *
+ * o is stored in BF16 and the last S in FP32.  The backward returns the
+ * gradients of <do, o> + <dfinal_state, S_final> with respect to the raw
+ * inputs, in the order dq, dk, dv, dg, dbeta, dA_log, ddt_bias, dinitial_state
+ * (page "flashinfer.kda_backward.recurrent_kda_backward", description).
+ *
+ * Tensor contract (page "flashinfer.kda_training.recurrent_kda_training_
+ * forward", parameters; page "flashinfer.kda_training", paragraphs 3-4).  All
+ * tensors are dense, row-major and contiguous, in device memory unless noted:
+ *     q, k, dq, dk            BF16  [B][T][Hqk][128]
+ *     v, g, o, do, dv, dg     BF16  [B][T][Hv][128]
+ *     beta, dbeta             BF16  [B][T][Hv]       (raw logits)
+ *     A_log, dA_log           FP32  [Hv]
+ *     dt_bias, ddt_bias       FP32  [Hv][128]
+ *     initial_state, final_state, dfinal_state, dinitial_state
+ *                             FP32  [N][Hv][128][128]   (value-first: [v][k])
+ * Fixed layout: N = B, every batch row is one sequence of T tokens, and both
+ * cu_seqlens pointers are NULL.  Packed layout: B = 1, sequence n occupies
+ * tokens [cu[n], cu[n+1]) of the single row; cu_seqlens (device, INT64 [N+1])
+ * and its trusted host mirror cu_seqlens_host (INT64 [N+1]) are both given.
+ * Every sequence is non-empty; lengths need not be multiples of 16.  Hv must
+ * be a multiple of Hqk.  scale is 1/sqrt(128) and lower_bound is -5.
+ *
+ * Ownership.  The caller owns every buffer: inputs, outputs, the forward
+ * context and the backward workspace.  The library keeps, per device, a cache
+ * of small device-side schedules keyed by the sequence lengths (as the pages
+ * cache their longest-first order per unchanged offsets), and a host-side
+ * record of each context's producing call for the backward's checks.
+ *
+ * Errors.  Every entry point returns a kda_status.  All argument checks run on
+ * the host before any launch; nothing is launched when a check fails.  A HIP
+ * failure after launches began returns KDA_ERR_HIP; kda_last_error() gives
+ * the text of the last failure on the calling thread.  Launches are
+ * asynchronous on the given stream (a hipStream_t; NULL is the null stream).
+ * No entry point synchronises the device.
+ */
+#ifndef LIBKDA_H
+#define LIBKDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128
+#define KDA_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_ARG = 1,       /* a required pointer is NULL */
+    KDA_ERR_SHAPE = 2,          /* B, T, heads, N out of range or inconsistent */
+    KDA_ERR_GROUPING = 3,       /* Hv is not a multiple of Hqk */
+    KDA_ERR_SEQLENS = 4,        /* cu_seqlens_host not 0 < ... strictly increasing ... = T */
+    KDA_ERR_SCALE = 5,          /* scale is neither 0 nor 1/sqrt(128) */
+    KDA_ERR_LOWER_BOUND = 6,    /* lower_bound is not -5 */
+    KDA_ERR_OVERLAP = 7,        /* an output overlaps an input, the context or another output */
+    KDA_ERR_CTX_SIZE = 8,       /* context smaller than kda_fwd_ctx_bytes() */
+    KDA_ERR_CTX_MISMATCH = 9,   /* context not produced by a matching kda_fwd */
+    KDA_ERR_WORKSPACE_SIZE = 10,/* workspace smaller than kda_bwd_workspace_bytes() */
+    KDA_ERR_ROUTE = 11,         /* unknown route or checkpoint interval */
+    KDA_ERR_HIP = 12            /* a HIP runtime call failed */
+} kda_status;
+
+typedef enum {
+    KDA_ROUTE_AUTO = 0,      /* library chooses */
+    KDA_ROUTE_CHUNK = 1,     /* chunked MFMA kernel */
+    KDA_ROUTE_ROWSPLIT = 2   /* per-token FP32 kernel, state rows split across workgroups */
+} kda_route;
+
+/* One call's shape.  All fields are read by value; the struct is not kept. */
+typedef struct {
+    int32_t B;                       /* physical batch (1 when packed) */
+    int32_t T;                       /* tokens per batch row */
+    int32_t Hqk;                     /* q/k heads */
+    int32_t Hv;                      /* value heads, a multiple of Hqk */
+    int32_t N;                       /* sequences: B (fixed) or len(cu_seqlens)-1 (packed) */
+    const int64_t* cu_seqlens;       /* device INT64 [N+1], or NULL for fixed layout */
+    const int64_t* cu_seqlens_host;  /* host INT64 [N+1] mirror, NULL iff cu_seqlens is NULL */
+    float scale;                     /* 0 selects 1/sqrt(128); any other value must equal it */
+    float lower_bound;               /* must be -5 */
+    int32_t route;                   /* kda_route; AUTO unless testing a route */
+    int32_t checkpoint_every;        /* tape interval in tokens; 0 selects 256; a multiple of 16 */
+} kda_problem;
+
+/* Library version (KDA_VERSION). */
+int kda_version(void);
+
+/* Static text for a status code. */
+const char* kda_status_string(kda_status status);
+
+/* Text of the last failure on this thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Bytes the forward context needs: the FP32 state tape saved for the
+ * backward (one [Hv][128][128] slab per sequence and per interval boundary
+ * strictly inside the sequence) plus alignment.  Validates the problem. */
+kda_status kda_fwd_ctx_bytes(const kda_problem* p, size_t* bytes);
+
+/* Bytes the backward workspace needs (chunk-start states rebuilt from the
+ * tape, FP32 partial sums).  Validates the problem. */
+kda_status kda_bwd_workspace_bytes(const kda_problem* p, size_t* bytes);
+
+/* Host planning only (no device access): the route the forward would take,
+ * the number of (sequence, value head) tasks, and optionally the task order
+ * (longest sequence first; each entry is n * Hv + h) into order[0..cap).
+ * Used by tests of the scheduler.  Page "flashinfer.kda.recurrent_kda",
+ * parameter cu_seqlens: longer sequences are scheduled first. */
+kda_status kda_plan_query(const kda_problem* p, int32_t* route, int64_t* num_tasks,
+                          int32_t* order, int64_t cap);
+
+/* Training forward (page "flashinfer.kda_training.recurrent_kda_training_
+ * forward").  Writes o and final_state, and, when ctx is not NULL, the state
+ * tape that kda_bwd consumes.  ctx may be NULL (ctx_bytes 0) when no backward
+ * will follow.  Outputs must not overlap inputs, ctx or each other
+ * ("flashinfer.kda_training", paragraph 1).  Asynchronous on `stream`. */
+kda_status kda_fwd(const kda_problem* p,
+                   const void* q, const void* k, const void* v, const void* g,
+                   const void* beta, const float* A_log, const float* dt_bias,
+                   const float* initial_state,
+                   void* o, float* final_state,
+                   void* ctx, size_t ctx_bytes, void* stream);
+
+/* Training backward (pages "flashinfer.kda_backward.recurrent_kda_backward"
+ * and "flashinfer.kda_training", paragraph 5).  Takes the same problem and
+ * input pointers as the kda_fwd that filled ctx (checked against the host
+ * record of that call, together with the device and the stream: a context is
+ * used on the stream that created it), the adjoints d_o and dfinal_state, and
+ * writes the eight gradients.  dq/dk sum over the value heads that share a
+ * q/k head; dA_log/ddt_bias sum over all sequences and tokens.  The
+ * workspace is caller-owned scratch of kda_bwd_workspace_bytes() bytes.
+ * Inputs must not have changed since the forward.  Asynchronous. */
+kda_status kda_bwd(const kda_problem* p,
+                   const void* q, const void* k, const void* v, const void* g,
+                   const void* beta, const float* A_log, const float* dt_bias,
+                   const float* initial_state,
+                   const void* ctx, size_t ctx_bytes,
+                   const void* d_o, const float* dfinal_state,
+                   void* dq, void* dk, void* dv, void* dg, void* dbeta,
+                   float* dA_log, float* ddt_bias, float* dinitial_state,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKDA_H */
