@@ -1,0 +1,173 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA training recurrence on one MI355X.
+
+Workload: packed 8 x 1024 tokens, Hqk = Hv = 96, K = V = 128 (synthetic,
+seeded; the FlashInfer page "flashinfer.kda_training" validates its kernels
+on this exact shape).  A step is one pass of the hot path over that batch:
+the training forward (o, final state and the FP32 state tape) followed by
+the backward (all eight gradients) when --no-bwd is not given.
+
+Printed: one JSON line with the forward throughput in token-heads/s (the
+headline), the forward and backward times per step, the roofline of the
+dominant kernel (the chunked forward) measured with HIP events on its own
+stream, and the FP64 oracle timed on this host's cores as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+
+
+def algorithmic_fwd_bytes(problem) -> int:
+    """Bytes the forward must move at least: q, k (shared by G heads), v, g,
+    beta, o per token-head, plus the initial and final FP32 state per task."""
+    toks = sum(problem.lengths)
+    G = problem.Hv // problem.Hqk
+    per_tok_head = 2 * 128 * 2 / G + 128 * 2 * 3 + 2
+    return int(toks * problem.Hv * per_tok_head + problem.N * problem.Hv * 2 * 128 * 128 * 4)
+
+
+def cpu_baseline(inp, max_seconds: float = 30.0):
+    import numpy as np
+    import oracle
+    p = inp.problem
+    workers = oracle.default_workers()
+    # bounded sample: whole sequences x heads until ~max_seconds of estimated work
+    est_per_tok_head = 60e-6
+    budget = max_seconds * workers
+    tasks = []
+    work = 0.0
+    for h in range(p.Hv):
+        for n in range(p.N):
+            if work >= budget:
+                break
+            tasks.append((n, h))
+            work += p.lengths[n] * est_per_tok_head
+    th = sum(p.lengths[n] for (n, h) in tasks)
+    t = time.perf_counter()
+    oracle.forward(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.A_log, inp.dt_bias,
+                   inp.initial_state, p.lengths, p.packed, tasks=tasks, workers=workers)
+    dt = time.perf_counter() - t
+    return {"value": th / dt, "unit": "token-heads/s", "cores": workers, "kind": "oracle",
+            "sample": f"FP64 oracle forward of {len(tasks)} of {p.N * p.Hv} (sequence, head) "
+                      f"tasks = {th} token-heads, {dt:.2f} s wall on {workers} processes"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="packed")
+    ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--route", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import gated_delta_rule_32_amd as kda
+
+    inp_cpu = workloads.make_workload(args.workload, with_adjoints=True)
+    p = inp_cpu.problem
+    d = inp_cpu.to("cuda")
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    prob = kda.make_problem(p.B, p.T, p.Hqk, p.Hv, p.N, d.cu_seqlens, inp_cpu.cu_seqlens,
+                            route=args.route)
+    route, ntasks, _ = kda.kda_plan_query(prob)
+    o = torch.empty_like(d.v)
+    fs = torch.empty_like(d.initial_state)
+    ctx = torch.empty(kda.kda_fwd_ctx_bytes(prob), dtype=torch.uint8, device=dev)
+    do_bwd = not args.no_bwd
+    if do_bwd:
+        ws = torch.empty(kda.kda_bwd_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+        grads = (torch.empty_like(d.q), torch.empty_like(d.k), torch.empty_like(d.v),
+                 torch.empty_like(d.g), torch.empty_like(d.beta), torch.empty_like(d.A_log),
+                 torch.empty_like(d.dt_bias), torch.empty_like(d.initial_state))
+    h = stream.cuda_stream
+
+    def fwd():
+        kda.kda_fwd(prob, d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
+                    o, fs, ctx, h)
+
+    def bwd():
+        kda.kda_bwd(prob, d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
+                    ctx, d.do, d.dfinal_state, *grads, ws, h)
+
+    for _ in range(args.warmup):
+        fwd()
+        if do_bwd:
+            bwd()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        if do_bwd:
+            bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
+    bwd_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
+    fwd_med = fwd_ms[len(fwd_ms) // 2]
+    fwd_mean = sum(fwd_ms) / len(fwd_ms)
+    bwd_med = bwd_ms[len(bwd_ms) // 2]
+    token_heads = p.token_heads
+    value = token_heads / (fwd_mean * 1e-3)
+    ms_per_step = wall * 1e3 / args.steps
+
+    algo = algorithmic_fwd_bytes(p)
+    achieved = algo / (fwd_mean * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "fwd_chunk_kernel" if route == 1 else "fwd_rowsplit_kernel",
+            "algorithmic_bytes_per_launch": algo, "avg_launch_ms": round(fwd_mean, 4)}
+    out = {
+        "metric": "KDA fwd token-heads/sec (packed 8x1024, 96 heads, 1 GPU)",
+        "value": round(value, 1),
+        "unit": "token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "fwd_ms_median": round(fwd_med, 4),
+        "fwd_ms_p10": round(fwd_ms[len(fwd_ms) // 10], 4),
+        "fwd_ms_p90": round(fwd_ms[(9 * len(fwd_ms)) // 10], 4),
+        "bwd_ms_median": round(bwd_med, 4) if do_bwd else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{p.name}: {p.N} sequences x {p.lengths[0] if p.name != 'mixed' else 'mixed'}"
+                               f" tokens, Hqk={p.Hqk}, Hv={p.Hv}, K=V=128",
+                   "token_heads": token_heads, "route": "chunk" if route == 1 else "rowsplit",
+                   "tape_interval": 256, "step": "fwd+bwd" if do_bwd else "fwd"},
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(inp_cpu)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
