@@ -8,20 +8,24 @@
 //   gc = cumsum(lam) over the chunk's tokens,  Gam = exp(gc),  gC = gc[last]
 //   Qg = qn*Gam,  Kg = kn*Gam,  Ki = kn/Gam,  Kt = kn*exp(gC - gc)
 //   Akk = strictly-lower(Kg Ki^T),  Aqk = lower(Qg Ki^T)
-//   Tb  = (I + diag(beta) Akk)^-1 diag(beta)        (forward substitution)
-//   W   = Tb Kg,   Ut = Tb V,   U = Ut - W S0^T
+//   Tb  = (I + diag(beta) Akk)^-1 diag(beta)        (substitution)
+//   Y   = Kg S0^T,   U = Tb V - Tb Y
 //   O   = scale (Qg S0^T + Aqk U)
 //   S_C = S0 diag(exp(gC)) + U^T Kt
 //
+// (U = Tb (V - Kg S0^T) is the chunk's delta-rule correction; forming Kg S0^T
+// first keeps it independent of the substitution, so its MFMAs overlap it.)
 // Within a chunk the log-decay sums stay above 16 * (-5) = -80, so the factors
 // exp(+-gc) stay inside the FP32/BF16 exponent range (e^80 < 3.4e38).
 //
 // Work split.  One workgroup (4 waves) owns one (sequence, value head) task
 // for its whole length; wave w owns state columns v in [32w, 32w+32), held as
 // transposed 16x16 frags S^T[kb][vb] in FP32 registers.  The state path is
-// column-local, so no state crosses waves; the chunk's shared operands pass
-// through LDS in "frag slots" (64 lanes x 4 bf16, padded against bank
-// conflicts):
+// column-local, so no state crosses waves.  Three barriers per chunk: after
+// the gate (the prefix sums need every row), after the prefix sums, and after
+// the chunk's shared operands are in LDS; from there each wave works alone
+// (it redoes the small 16x16 algebra itself rather than wait for another).
+// Shared operands sit in LDS "frag slots" (64 lanes x 4 bf16, padded):
 //   RF(X)[kb]: lane (gq, c) holds X[c][16kb + 4gq + i]   (rows = tokens)
 //   CF(X)[kb]: lane (gq, k) holds X[4gq + i][16kb + k]   (tokens along i)
 // Products that contract over tokens take CF operands, those that contract
@@ -30,17 +34,12 @@
 // consecutive channels of one token, stored straight to global memory.
 //
 // Precision.  Only the products that add new information to the carried state
-// need FP32-accurate operands: Ut = Tb V (Tb as a BF16 hi/lo pair, V exact)
-// and U^T Kt (both operands as hi/lo pairs, three products).  W, W S0^T, the
-// A matrices and the output product use plain BF16 operands: the delta rule
-// re-measures the state against each key, so rounding in the prediction
-// W S0^T does not accumulate (checked against the FP64 definition over
-// 1024-4096-token sequences: final-state error ~2e-5 to 5e-5).
-//
-// Latency.  The next chunk's inputs are loaded into the same registers right
-// after their last use (end of phase C), so they arrive during the rest of the
-// chunk without a second register buffer or a register copy; vector-memory
-// waits then fall only on the first use, at the start of the next chunk.
+// need FP32-accurate operands: Tb V (Tb as a BF16 hi/lo pair, V exact) and
+// U^T Kt (both operands as hi/lo pairs, three products).  Kg S0^T, Tb Y, the A
+// matrices and the output use plain BF16 operands: the delta rule re-measures
+// the state against each key, so rounding in the prediction does not
+// accumulate (checked against the FP64 definition over 1024-4096-token
+// sequences: final-state error ~2e-5 to 5e-5).
 #include "kda_common.hpp"
 #include "kda_kernels.h"
 
@@ -50,23 +49,25 @@ namespace {
 
 constexpr int FC_THREADS = 256;
 constexpr int FS = 264;  // frag slot stride in bf16 (256 + 8 padding)
+constexpr int TBS = 20;  // row stride of the per-wave Tb scratch (16-byte rows)
+
+struct WaveScratch {         // private to one wave: no barrier between its uses
+    float nT[CH][CH];        // nT[m][i] = beta_i Akk[i][m] for i > m, else 0
+    float tb[CH][TBS];       // Tb[i][j]
+};
 
 struct FwdLds {
     float lam[CH][D];        // log2-domain decays, then their in-chunk prefix sums
     float gamc[D];           // exp(gC) per channel
     float dtz[D];            // dt_bias * exp(A_log) * log2(e)
-    float beta[CH];
-    float akkT[CH][CH];      // akkT[m][i] = Akk[i][m] (strictly lower part)
+    float beta[2][CH];       // double-buffered: a wave may start the next chunk
+                             // while another still solves with this one's
+    WaveScratch pw[4];
     bf16 rf_qg[8 * FS];
     bf16 rf_kg[8 * FS];
     bf16 rf_ki[8 * FS];
-    bf16 cf_kg[8 * FS];
     bf16 cf_kth[8 * FS];
     bf16 cf_ktl[8 * FS];
-    bf16 rf_w[8 * FS];       // RF(-W)
-    bf16 tbh[FS];            // RF16(Tb): lane (gq, c) holds Tb[c][4gq+i]
-    bf16 tbl[FS];
-    bf16 aqk[FS];            // RF16(Aqk)
 };
 
 __device__ __forceinline__ int rf_off(int c, int k) {  // (token c, channel k) in an RF slot set
@@ -77,9 +78,6 @@ __device__ __forceinline__ int cf_off(int c, int k) {  // (token c, channel k) i
 }
 __device__ __forceinline__ bf16x4 ld4(const bf16* slot, int lane) {
     return *(const bf16x4*)(slot + lane * 4);
-}
-__device__ __forceinline__ void st4(bf16* slot, int lane, bf16x4 x) {
-    *(bf16x4*)(slot + lane * 4) = x;
 }
 
 struct RowIn {   // one token row, 8 channels (row-owner mapping)
@@ -117,6 +115,46 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], 
             *(float4*)(dst + (int64_t)vcol * D + 16 * kb + 4 * gq) =
                 make_float4(S[kb][j][0], S[kb][j][1], S[kb][j][2], S[kb][j][3]);
         }
+}
+
+// Column-layout stores of one 4-channel group for a pair of token rows.
+// Rows c (even) and c+1 sit in lane rows 2p and 2p+1 of the wave; after one
+// lane-row swap the even row's lanes hold both rows' values for channels
+// c8+4..c8+7 and the odd row's lanes for c8..c8+3, so each lane writes four
+// (row c, row c+1) pairs as 32-bit words (the two rows are adjacent in CF).
+__device__ __forceinline__ void store_cf_pairs(bf16* slots, int r, int c8, bf16x4 lo, bf16x4 hi) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 ulo = __builtin_bit_cast(u32x2, lo);
+    const u32x2 uhi = __builtin_bit_cast(u32x2, hi);
+    // swap(a = hi, b = lo): lane row 2p receives row 2p+1's `hi` in the second
+    // result, lane row 2p+1 receives row 2p's `lo` in the first.
+    const auto s0 = __builtin_amdgcn_permlane16_swap(uhi[0], ulo[0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(uhi[1], ulo[1], false, false);
+    const bool even = (r & 1) == 0;
+    const u32x2 part = even ? u32x2{s0[1], s1[1]} : u32x2{s0[0], s1[0]};
+    const bf16x4 p = __builtin_bit_cast(bf16x4, part);
+    const bf16x4 m = even ? hi : lo;
+    const int kbase = c8 + (even ? 4 : 0);
+    const int o = cf_off(r & ~1, kbase);  // channel kbase + j sits at o + 4j
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        bf16x2 pr;
+        pr[0] = even ? m[j] : p[j];
+        pr[1] = even ? p[j] : m[j];
+        *(bf16x2*)&slots[o + 4 * j] = pr;
+    }
+}
+
+// Broadcast lane q of every quad to the whole quad (DPP quad_perm [q,q,q,q]);
+// q must fold to a constant.
+__device__ __forceinline__ float quad_bcast(float x, int q) {
+    const int xi = __float_as_int(x);
+    switch (q) {
+        case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0x00, 0xF, 0xF, false));
+        case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0x55, 0xF, 0xF, false));
+        case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0xAA, 0xF, 0xF, false));
+        default: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0xFF, 0xF, 0xF, false));
+    }
 }
 
 }  // namespace
@@ -191,8 +229,8 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 sq += qv * qv;
                 sk += kv * kv;
             }
-            sq = group_sum<16>(sq);
-            sk = group_sum<16>(sk);
+            sq = row16_sum(sq);
+            sk = row16_sum(sk);
             rq = valid ? fast_rsqrt(sq + 1e-6f) : 0.f;
             rk = valid ? fast_rsqrt(sk + 1e-6f) : 0.f;
             float lv[8], dz[8];
@@ -205,7 +243,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             }
             *(float4*)&sm.lam[r][c8] = make_float4(lv[0], lv[1], lv[2], lv[3]);
             *(float4*)&sm.lam[r][c8 + 4] = make_float4(lv[4], lv[5], lv[6], lv[7]);
-            if ((tix & 15) == 0) sm.beta[r] = valid ? sigmoidf_((float)cur.b) : 0.f;
+            if ((tix & 15) == 0) sm.beta[ci & 1][r] = valid ? sigmoidf_((float)cur.b) : 0.f;
         }
         __syncthreads();
         // ---- B: prefix sums over the chunk's tokens, per channel ----
@@ -226,24 +264,20 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             *(float4*)&gc[4] = *(const float4*)&sm.lam[r][c8 + 4];
             *(float4*)&gC[0] = *(const float4*)&sm.gamc[c8];
             *(float4*)&gC[4] = *(const float4*)&sm.gamc[c8 + 4];
-            bf16x4 qg4[2], kg4[2], ki4[2];
-            const int ocf = cf_off(r, c8);  // channel c8 + i sits at ocf + 4i
+            bf16x4 qg4[2], kg4[2], ki4[2], th4[2], tl4[2];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float qn = (float)cur.q[i] * rq;
                 const float kn = (float)cur.k[i] * rk;
                 const float gam = __builtin_amdgcn_exp2f(gc[i]);
                 const float gin = __builtin_amdgcn_exp2f(-gc[i]);
-                const float kg = kn * gam;
                 const float kt = kn * gin * gC[i];
                 qg4[i >> 2][i & 3] = (bf16)(qn * gam);
-                const bf16 kgb = (bf16)kg;
-                kg4[i >> 2][i & 3] = kgb;
+                kg4[i >> 2][i & 3] = (bf16)(kn * gam);
                 ki4[i >> 2][i & 3] = (bf16)(kn * gin);
                 const bf16 kth = (bf16)kt;
-                sm.cf_kg[ocf + 4 * i] = kgb;
-                sm.cf_kth[ocf + 4 * i] = kth;
-                sm.cf_ktl[ocf + 4 * i] = (bf16)(kt - (float)kth);
+                th4[i >> 2][i & 3] = kth;
+                tl4[i >> 2][i & 3] = (bf16)(kt - (float)kth);
             }
             const int orf = rf_off(r, c8);  // channels c8+4.. sit one lane group later
 #pragma unroll
@@ -252,118 +286,109 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 *(bf16x4*)&sm.rf_kg[orf + 64 * s] = kg4[s];
                 *(bf16x4*)&sm.rf_ki[orf + 64 * s] = ki4[s];
             }
+            store_cf_pairs(sm.cf_kth, r, c8, th4[0], th4[1]);
+            store_cf_pairs(sm.cf_ktl, r, c8, tl4[0], tl4[1]);
         }
         // the row inputs are dead: fetch the next chunk's into the same registers
         load_rows(cur, a, tok0 + min(t0 + CH + r, L - 1), hq, h, c8);
         __syncthreads();
-        // ---- D: V to CF (all); Akk and the substitution (wave 0); Aqk (wave 1) ----
-        bf16x4 cfv[2];
+
+        // ---- D: per wave.  N = diag(beta) Akk into the wave's scratch ----
+        WaveScratch& ws = sm.pw[wave];
         {
-            bf16x4 ident;  // frag of the 16x16 identity: lane (gq, n) holds I[4gq+i][n]
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ident[i] = (bf16)((4 * gq + i == cl) ? 1.0f : 0.0f);
-            // CF(V)[vb] = RF(V)[vb] * I, exact
-            cfv[0] = to_bf4(mma16(vcur.v0, ident, zero4()));
-            cfv[1] = to_bf4(mma16(vcur.v1, ident, zero4()));
-        }
-        load_cols(vcur, a, tok0 + min(t0 + CH + cl, L - 1), h, 32 * wave + 4 * gq);
-        if (wave == 0) {
-            f32x4 acc = zero4();
+            f32x4 akk = zero4();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bf16x8 x = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
-                const bf16x8 y = cat8(ld4(&sm.rf_ki[(2 * j) * FS], lane), ld4(&sm.rf_ki[(2 * j + 1) * FS], lane));
-                acc = mma32(x, y, acc);
+                const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
+                const bf16x8 ki8 = cat8(ld4(&sm.rf_ki[(2 * j) * FS], lane), ld4(&sm.rf_ki[(2 * j + 1) * FS], lane));
+                akk = mma32(kg8, ki8, akk);     // lane (gq, c) holds Akk[4gq+i][c]
             }
-            // lane (gq, cl) holds Akk[4gq+i][cl]: store column cl, rows 4gq..4gq+3
-            {
-                float4 col;
-                col.x = (cl < 4 * gq + 0) ? acc[0] : 0.f;
-                col.y = (cl < 4 * gq + 1) ? acc[1] : 0.f;
-                col.z = (cl < 4 * gq + 2) ? acc[2] : 0.f;
-                col.w = (cl < 4 * gq + 3) ? acc[3] : 0.f;
-                *(float4*)&sm.akkT[cl][4 * gq] = col;
-            }
-            if (lane < 16) {
-                // Column `lane` of T by right-looking substitution: once t[m]
-                // is final, every later row takes its share of it.
-                //   t[i] = [i == col] - beta_i * sum_{m<i} Akk[i][m] t[m]
-                const int col = lane;
-                float acc_t[CH];
-#pragma unroll
-                for (int i = 0; i < CH; ++i) acc_t[i] = 0.f;
-                float t[CH];
-#pragma unroll
-                for (int m = 0; m < CH; ++m) {
-                    const float tm = (m == col) ? 1.0f : -sm.beta[m] * acc_t[m];
-                    t[m] = tm;
-                    if (m + 1 < CH) {
-                        float ac[CH];
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4)
-                            if (4 * q4 + 3 > m) *(float4*)&ac[4 * q4] = *(const float4*)&sm.akkT[m][4 * q4];
-#pragma unroll
-                        for (int i = m + 1; i < CH; ++i) acc_t[i] += ac[i] * tm;
-                    }
-                }
-                const float bc = sm.beta[col];
-#pragma unroll
-                for (int i = 0; i < CH; ++i) {
-                    const float x = t[i] * bc;  // Tb[i][col]
-                    const bf16 xh = (bf16)x;
-                    const int o = (((col >> 2) << 4) + i) * 4 + (col & 3);
-                    sm.tbh[o] = xh;
-                    sm.tbl[o] = (bf16)(x - (float)xh);
-                }
-            }
-        } else if (wave == 1) {
-            // Aqk^T = Ki Qg^T: lane (gq, c) holds Aqk[c][4gq+i] = RF16(Aqk)
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 x = cat8(ld4(&sm.rf_ki[(2 * j) * FS], lane), ld4(&sm.rf_ki[(2 * j + 1) * FS], lane));
-                const bf16x8 y = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
-                acc = mma32(x, y, acc);
-            }
-            bf16x4 x;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[i] = (bf16)((4 * gq + i <= cl) ? acc[i] : 0.f);
-            st4(sm.aqk, lane, x);
+            const float4 b4 = *(const float4*)&sm.beta[ci & 1][4 * gq];
+            float4 col;  // column cl of N, rows 4gq..4gq+3
+            col.x = (cl < 4 * gq + 0) ? b4.x * akk[0] : 0.f;
+            col.y = (cl < 4 * gq + 1) ? b4.y * akk[1] : 0.f;
+            col.z = (cl < 4 * gq + 2) ? b4.z * akk[2] : 0.f;
+            col.w = (cl < 4 * gq + 3) ? b4.w * akk[3] : 0.f;
+            *(float4*)&ws.nT[cl][4 * gq] = col;
         }
-        __syncthreads();
-        // ---- E: -W frags (kb = 2w, 2w+1) and Ut for the wave's columns ----
-        f32x4 U[2];
-        {
-            const bf16x4 tbh = ld4(sm.tbh, lane);
-            const bf16x4 tbl = ld4(sm.tbl, lane);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int kb = 2 * wave + j;
-                // W^T[kb] = Kg^T Tb^T: A = CF(Kg)[kb], B = RF16(Tb)
-                const f32x4 w = mma16(ld4(&sm.cf_kg[kb * FS], lane), tbh, zero4());
-                st4(&sm.rf_w[kb * FS], lane, to_bf4(-w));
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                U[j] = mma16(tbh, cfv[j], zero4());
-                U[j] = mma16(tbl, cfv[j], U[j]);
-            }
-        }
-        __syncthreads();
-        // ---- F: U = Ut - W S0^T;  O^T = S0 Qg^T + U^T Aqk^T;  S update ----
+        // Y = Kg S0^T and O^T = S0 Qg^T: independent of the substitution
+        f32x4 Y[2] = {zero4(), zero4()};
         f32x4 OT[2] = {zero4(), zero4()};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bf16x8 w8 = cat8(ld4(&sm.rf_w[(2 * j) * FS], lane), ld4(&sm.rf_w[(2 * j + 1) * FS], lane));
+            const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
             const bf16x8 q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb) {
                 const bf16x8 s8 = cat8(to_bf4(S[2 * j][vb]), to_bf4(S[2 * j + 1][vb]));
-                U[vb] = mma32(w8, s8, U[vb]);
-                OT[vb] = mma32(s8, q8, OT[vb]);
+                Y[vb] = mma32(kg8, s8, Y[vb]);    // lane (gq, v) holds Y[4gq+i][v]
+                OT[vb] = mma32(s8, q8, OT[vb]);   // lane (gq, c) holds O[c][v=4gq+i]
             }
         }
-        const bf16x4 aq = ld4(sm.aqk, lane);
+        // T = (I + N)^-1 by right-looking substitution on all 64 lanes: lane
+        // (col = lane/4, q = lane%4) keeps rows 4q..4q+3 of column col.  Step m
+        // finalizes row m (in the quad lane q = m/4), broadcasts it inside the
+        // quad, and every lane subtracts its rows' share N[i][m] t[m] (N is
+        // zero on and above the diagonal, so no masking is needed).
+        {
+            const int col = lane >> 2;
+            const int qd = lane & 3;
+            float x[4] = {0.f, 0.f, 0.f, 0.f};
+            float4 nxt = *(const float4*)&ws.nT[0][4 * qd];
+#pragma unroll
+            for (int m = 0; m < CH; ++m) {
+                const float4 nm = nxt;
+                if (m + 1 < CH) nxt = *(const float4*)&ws.nT[m + 1][4 * qd];
+                const float cand = (m == col) ? 1.0f : -x[m & 3];
+                const float tm = quad_bcast(cand, m >> 2);
+                if (qd == (m >> 2)) x[m & 3] = tm;
+                x[0] += nm.x * tm;
+                x[1] += nm.y * tm;
+                x[2] += nm.z * tm;
+                x[3] += nm.w * tm;
+            }
+            // Tb[i][col] = T[i][col] beta_col
+            const float bc = sm.beta[ci & 1][col];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ws.tb[4 * qd + j][col] = x[j] * bc;
+        }
+        // RF16(Tb) as a hi/lo pair: lane (gq, c) holds Tb[c][4gq+i]
+        bf16x4 tbh, tbl;
+        {
+            const float4 t4 = *(const float4*)&ws.tb[cl][4 * gq];
+            split4(f32x4{t4.x, t4.y, t4.z, t4.w}, tbh, tbl);
+        }
+        // RF16(Aqk) = frag of Aqk^T = Ki Qg^T, causal part
+        bf16x4 aq;
+        {
+            f32x4 aqkT = zero4();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 ki8 = cat8(ld4(&sm.rf_ki[(2 * j) * FS], lane), ld4(&sm.rf_ki[(2 * j + 1) * FS], lane));
+                const bf16x8 qg8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
+                aqkT = mma32(ki8, qg8, aqkT);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) aq[i] = (bf16)((4 * gq + i <= cl) ? aqkT[i] : 0.f);
+        }
+        // CF(V) for the wave's columns (RF(V) times the identity, exact), then
+        // U = Tb V - Tb Y
+        f32x4 U[2];
+        {
+            bf16x4 ident;  // lane (gq, n) holds I[4gq+i][n]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ident[i] = (bf16)((4 * gq + i == cl) ? 1.0f : 0.0f);
+            const bf16x4 cfv0 = to_bf4(mma16(vcur.v0, ident, zero4()));
+            const bf16x4 cfv1 = to_bf4(mma16(vcur.v1, ident, zero4()));
+            U[0] = mma16(tbh, cfv0, zero4());
+            U[0] = mma16(tbl, cfv0, U[0]);
+            U[0] = mma16(tbh, to_bf4(-Y[0]), U[0]);
+            U[1] = mma16(tbh, cfv1, zero4());
+            U[1] = mma16(tbl, cfv1, U[1]);
+            U[1] = mma16(tbh, to_bf4(-Y[1]), U[1]);
+        }
+        load_cols(vcur, a, tok0 + min(t0 + CH + cl, L - 1), h, 32 * wave + 4 * gq);
+        // O^T += U^T Aqk^T, store; then S update
         bf16x4 uh[2], ul[2];
 #pragma unroll
         for (int vb = 0; vb < 2; ++vb) {
