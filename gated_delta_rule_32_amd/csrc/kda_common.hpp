@@ -58,20 +58,25 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
 }
 
 __device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
-    bf16x4 r;
-    r[0] = (bf16)x[0]; r[1] = (bf16)x[1]; r[2] = (bf16)x[2]; r[3] = (bf16)x[3];
-    return r;
+    return __builtin_convertvector(x, bf16x4);  // two v_cvt_pk_bf16_f32
 }
-// FP32 x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): the pair carries
-// about 16 significant bits, so hi*hi' + hi*lo' + lo*hi' reproduces an FP32
-// product to ~2^-16 relative.
+__device__ __forceinline__ f32x4 from_bf4(bf16x4 x) {
+    return __builtin_convertvector(x, f32x4);
+}
+// FP32 x ~= hi + lo as a BF16 pair: hi keeps the top 16 bits of x (sign,
+// exponent, 7 mantissa bits; truncated), lo = bf16(x - hi) where x - hi is
+// exact.  The pair carries about 16 significant bits, so hi*hi' + hi*lo' +
+// lo*hi' reproduces an FP32 product to ~2^-16 relative.
 __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        bf16 h = (bf16)x[i];
-        hi[i] = h;
-        lo[i] = (bf16)(x[i] - (float)h);
-    }
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x4 u = __builtin_bit_cast(u32x4, x) & 0xffff0000u;
+    const f32x4 h = __builtin_bit_cast(f32x4, u);
+    // upper halves of (u0, u1) and (u2, u3) packed as bf16 pairs
+    const u32x2 hp = {__builtin_amdgcn_perm(u[1], u[0], 0x07060302u),
+                      __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
+    hi = __builtin_bit_cast(bf16x4, hp);
+    lo = to_bf4(x - h);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }

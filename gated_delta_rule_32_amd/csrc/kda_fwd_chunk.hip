@@ -40,6 +40,8 @@
 // the state against each key, so rounding in the prediction does not
 // accumulate (checked against the FP64 definition over 1024-4096-token
 // sequences: final-state error ~2e-5 to 5e-5).
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_kernels.h"
 
@@ -52,22 +54,22 @@ constexpr int FS = 264;  // frag slot stride in bf16 (256 + 8 padding)
 constexpr int TBS = 20;  // row stride of the per-wave Tb scratch (16-byte rows)
 
 struct WaveScratch {         // private to one wave: no barrier between its uses
-    float nT[CH][CH];        // nT[m][i] = beta_i Akk[i][m] for i > m, else 0
-    float tb[CH][TBS];       // Tb[i][j]
+    alignas(16) float nT[CH][CH];   // nT[m][i] = beta_i Akk[i][m] for i > m, else 0
+    alignas(16) float tb[CH][TBS];  // Tb[i][j]
 };
 
 struct FwdLds {
-    float lam[CH][D];        // log2-domain decays, then their in-chunk prefix sums
-    float gamc[D];           // exp(gC) per channel
-    float dtz[D];            // dt_bias * exp(A_log) * log2(e)
-    float beta[2][CH];       // double-buffered: a wave may start the next chunk
-                             // while another still solves with this one's
+    alignas(16) float lam[CH][D];   // log2-domain decays, then their in-chunk prefix sums
+    alignas(16) float gamc[D];      // exp(gC) per channel
+    alignas(16) float dtz[D];       // dt_bias * exp(A_log) * log2(e)
+    alignas(16) float beta[2][CH];  // double-buffered: a wave may start the next
+                                    // chunk while another still solves with this one's
     WaveScratch pw[4];
-    bf16 rf_qg[8 * FS];
-    bf16 rf_kg[8 * FS];
-    bf16 rf_ki[8 * FS];
-    bf16 cf_kth[8 * FS];
-    bf16 cf_ktl[8 * FS];
+    alignas(16) bf16 rf_qg[8 * FS];
+    alignas(16) bf16 rf_kg[8 * FS];
+    alignas(16) bf16 rf_ki[8 * FS];
+    alignas(16) bf16 cf_kth[8 * FS];
+    alignas(16) bf16 cf_ktl[8 * FS];
 };
 
 __device__ __forceinline__ int rf_off(int c, int k) {  // (token c, channel k) in an RF slot set
@@ -131,18 +133,18 @@ __device__ __forceinline__ void store_cf_pairs(bf16* slots, int r, int c8, bf16x
     const auto s0 = __builtin_amdgcn_permlane16_swap(uhi[0], ulo[0], false, false);
     const auto s1 = __builtin_amdgcn_permlane16_swap(uhi[1], ulo[1], false, false);
     const bool even = (r & 1) == 0;
-    const u32x2 part = even ? u32x2{s0[1], s1[1]} : u32x2{s0[0], s1[0]};
-    const bf16x4 p = __builtin_bit_cast(bf16x4, part);
-    const bf16x4 m = even ? hi : lo;
+    const u32x2 p = even ? u32x2{s0[1], s1[1]} : u32x2{s0[0], s1[0]};
+    const u32x2 m = even ? uhi : ulo;
+    // (even-row value, odd-row value) pairs: the even row's bf16 goes to the
+    // low half; byte selectors for the low / high bf16 of each source word
+    const unsigned sel_lo = even ? 0x05040100u : 0x01000504u;
+    const unsigned sel_hi = even ? 0x07060302u : 0x03020706u;
     const int kbase = c8 + (even ? 4 : 0);
-    const int o = cf_off(r & ~1, kbase);  // channel kbase + j sits at o + 4j
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        bf16x2 pr;
-        pr[0] = even ? m[j] : p[j];
-        pr[1] = even ? p[j] : m[j];
-        *(bf16x2*)&slots[o + 4 * j] = pr;
-    }
+    unsigned* dst = (unsigned*)&slots[cf_off(r & ~1, kbase)];  // channel kbase+j at +2j words
+    dst[0] = __builtin_amdgcn_perm(p[0], m[0], sel_lo);
+    dst[2] = __builtin_amdgcn_perm(p[0], m[0], sel_hi);
+    dst[4] = __builtin_amdgcn_perm(p[1], m[1], sel_lo);
+    dst[6] = __builtin_amdgcn_perm(p[1], m[1], sel_hi);
 }
 
 // Broadcast lane q of every quad to the whole quad (DPP quad_perm [q,q,q,q]);
@@ -154,6 +156,16 @@ __device__ __forceinline__ float quad_bcast(float x, int q) {
         case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0x55, 0xF, 0xF, false));
         case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0xAA, 0xF, 0xF, false));
         default: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0xFF, 0xF, 0xF, false));
+    }
+}
+
+__device__ __forceinline__ void set_prio_by_remaining(int left, int total) {
+    const int p = (4 * left - 1) / total;  // 3 for the first quarter, 0 for the last
+    switch (p) {
+        case 3: __builtin_amdgcn_s_setprio(3); break;
+        case 2: __builtin_amdgcn_s_setprio(2); break;
+        case 1: __builtin_amdgcn_s_setprio(1); break;
+        default: __builtin_amdgcn_s_setprio(0); break;
     }
 }
 
@@ -204,10 +216,13 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     __syncthreads();
 
     const int nchunks = (L + CH - 1) / CH;
-    for (int ci = 0; ci < nchunks; ++ci) {
-        // Per-lane index arithmetic is recomputed every iteration from an
-        // opaque copy of the thread id; hoisted out of the loop it would keep
-        // ~20 address registers alive and push the kernel into scratch spills.
+    const int nfull = L / CH;
+    // One chunk; full chunks are compiled without the tail masks.
+    auto chunk = [&](const int ci, auto tail_tag) __attribute__((always_inline)) {
+        constexpr bool kTail = decltype(tail_tag)::value;
+        // Per-lane index arithmetic is recomputed every chunk from an opaque
+        // copy of the thread id; hoisted out of the loop it would keep ~20
+        // address registers alive and push the kernel into scratch spills.
         int tix = tid;
         asm volatile("" : "+v"(tix));
         const int lane = tix & 63;
@@ -216,11 +231,16 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         const int r = tix >> 4;          // row-owner mapping: token row r,
         const int c8 = (tix & 15) * 8;   // channels [c8, c8 + 8)
         const int t0 = ci * CH;
-        const int nv = min(CH, L - t0);
-        const bool valid = r < nv;
+        const int nv = kTail ? L - t0 : CH;
+        const bool valid = !kTail || r < nv;
+        // Issue priority by work left: the wave scheduler favours older
+        // waves, so without this the first workgroup on a CU races ahead and
+        // the last one finishes alone; raising the priority of those with
+        // more chunks left keeps co-resident tasks abreast.
+        set_prio_by_remaining(nchunks - ci, nchunks);
 
         // ---- A: norms, gate, beta ----
-        float rq, rk;
+        float rq, rk;   // 1/sqrt(128)/|q| and 1/|k| (zero for rows past the end)
         {
             float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -231,7 +251,8 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             }
             sq = row16_sum(sq);
             sk = row16_sum(sk);
-            rq = valid ? fast_rsqrt(sq + 1e-6f) : 0.f;
+            // the output scale rides on the query norm: O = (s Qg) S0^T + (s Aqk) U
+            rq = valid ? a.scale * fast_rsqrt(sq + 1e-6f) : 0.f;
             rk = valid ? fast_rsqrt(sk + 1e-6f) : 0.f;
             float lv[8], dz[8];
             *(float4*)&dz[0] = *(const float4*)&sm.dtz[c8];
@@ -243,18 +264,18 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             }
             *(float4*)&sm.lam[r][c8] = make_float4(lv[0], lv[1], lv[2], lv[3]);
             *(float4*)&sm.lam[r][c8 + 4] = make_float4(lv[4], lv[5], lv[6], lv[7]);
-            if ((tix & 15) == 0) sm.beta[ci & 1][r] = valid ? sigmoidf_((float)cur.b) : 0.f;
+            if ((tid & 15) == 0) sm.beta[ci & 1][r] = valid ? sigmoidf_((float)cur.b) : 0.f;
         }
         __syncthreads();
         // ---- B: prefix sums over the chunk's tokens, per channel ----
-        if (tix < D) {
+        if (tid < D) {
             float acc = 0.f;
 #pragma unroll
             for (int rr = 0; rr < CH; ++rr) {
-                acc += sm.lam[rr][tix];
-                sm.lam[rr][tix] = acc;
+                acc += sm.lam[rr][tid];
+                sm.lam[rr][tid] = acc;
             }
-            sm.gamc[tix] = __builtin_amdgcn_exp2f(acc);
+            sm.gamc[tid] = __builtin_amdgcn_exp2f(acc);
         }
         __syncthreads();
         // ---- C: decay factors and the chunk's operands ----
@@ -266,18 +287,24 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             *(float4*)&gC[4] = *(const float4*)&sm.gamc[c8 + 4];
             bf16x4 qg4[2], kg4[2], ki4[2], th4[2], tl4[2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float qn = (float)cur.q[i] * rq;
-                const float kn = (float)cur.k[i] * rk;
-                const float gam = __builtin_amdgcn_exp2f(gc[i]);
-                const float gin = __builtin_amdgcn_exp2f(-gc[i]);
-                const float kt = kn * gin * gC[i];
-                qg4[i >> 2][i & 3] = (bf16)(qn * gam);
-                kg4[i >> 2][i & 3] = (bf16)(kn * gam);
-                ki4[i >> 2][i & 3] = (bf16)(kn * gin);
-                const bf16 kth = (bf16)kt;
-                th4[i >> 2][i & 3] = kth;
-                tl4[i >> 2][i & 3] = (bf16)(kt - (float)kth);
+            for (int s4 = 0; s4 < 2; ++s4) {
+                f32x4 qg, kg, ki, kt;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 4 * s4 + j;
+                    const float qn = (float)cur.q[i] * rq;
+                    const float kn = (float)cur.k[i] * rk;
+                    const float gam = __builtin_amdgcn_exp2f(gc[i]);
+                    const float gin = __builtin_amdgcn_exp2f(-gc[i]);
+                    qg[j] = qn * gam;
+                    kg[j] = kn * gam;
+                    ki[j] = kn * gin;
+                    kt[j] = ki[j] * gC[i];
+                }
+                qg4[s4] = to_bf4(qg);
+                kg4[s4] = to_bf4(kg);
+                ki4[s4] = to_bf4(ki);
+                split4(kt, th4[s4], tl4[s4]);
             }
             const int orf = rf_off(r, c8);  // channels c8+4.. sit one lane group later
 #pragma unroll
@@ -326,31 +353,32 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             }
         }
         // T = (I + N)^-1 by right-looking substitution on all 64 lanes: lane
-        // (col = lane/4, q = lane%4) keeps rows 4q..4q+3 of column col.  Step m
-        // finalizes row m (in the quad lane q = m/4), broadcasts it inside the
-        // quad, and every lane subtracts its rows' share N[i][m] t[m] (N is
-        // zero on and above the diagonal, so no masking is needed).
+        // (col = lane/4, q = lane%4) keeps rows 4q..4q+3 of column col; N is
+        // zero on and above the diagonal, so no masking is needed.
         {
+            // y[j] (row 4q+j of column col) starts at [row == col] and loses
+            // N[row][m] t[m] at every step m; row m is final when step m
+            // begins, so t[m] = y of the quad lane that holds row m.
             const int col = lane >> 2;
             const int qd = lane & 3;
-            float x[4] = {0.f, 0.f, 0.f, 0.f};
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = (4 * qd + j == col) ? 1.0f : 0.0f;
             float4 nxt = *(const float4*)&ws.nT[0][4 * qd];
 #pragma unroll
             for (int m = 0; m < CH; ++m) {
                 const float4 nm = nxt;
                 if (m + 1 < CH) nxt = *(const float4*)&ws.nT[m + 1][4 * qd];
-                const float cand = (m == col) ? 1.0f : -x[m & 3];
-                const float tm = quad_bcast(cand, m >> 2);
-                if (qd == (m >> 2)) x[m & 3] = tm;
-                x[0] += nm.x * tm;
-                x[1] += nm.y * tm;
-                x[2] += nm.z * tm;
-                x[3] += nm.w * tm;
+                const float tm = quad_bcast(y[m & 3], m >> 2);
+                y[0] -= nm.x * tm;
+                y[1] -= nm.y * tm;
+                y[2] -= nm.z * tm;
+                y[3] -= nm.w * tm;
             }
             // Tb[i][col] = T[i][col] beta_col
             const float bc = sm.beta[ci & 1][col];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ws.tb[4 * qd + j][col] = x[j] * bc;
+            for (int j = 0; j < 4; ++j) ws.tb[4 * qd + j][col] = y[j] * bc;
         }
         // RF16(Tb) as a hi/lo pair: lane (gq, c) holds Tb[c][4gq+i]
         bf16x4 tbh, tbl;
@@ -368,16 +396,19 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 const bf16x8 qg8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
                 aqkT = mma32(ki8, qg8, aqkT);
             }
+            f32x4 am;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) aq[i] = (bf16)((4 * gq + i <= cl) ? aqkT[i] : 0.f);
+            for (int i = 0; i < 4; ++i) am[i] = (4 * gq + i <= cl) ? aqkT[i] : 0.f;
+            aq = to_bf4(am);
         }
         // CF(V) for the wave's columns (RF(V) times the identity, exact), then
         // U = Tb V - Tb Y
         f32x4 U[2];
         {
-            bf16x4 ident;  // lane (gq, n) holds I[4gq+i][n]
+            f32x4 id;  // lane (gq, n) holds I[4gq+i][n]
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ident[i] = (bf16)((4 * gq + i == cl) ? 1.0f : 0.0f);
+            for (int i = 0; i < 4; ++i) id[i] = (4 * gq + i == cl) ? 1.0f : 0.0f;
+            const bf16x4 ident = to_bf4(id);
             const bf16x4 cfv0 = to_bf4(mma16(vcur.v0, ident, zero4()));
             const bf16x4 cfv1 = to_bf4(mma16(vcur.v1, ident, zero4()));
             U[0] = mma16(tbh, cfv0, zero4());
@@ -396,9 +427,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             OT[vb] = mma16(uh[vb], aq, OT[vb]);
             // lane (gq, c) holds O[c][32w + 16vb + 4gq + i]
             if (cl < nv) {
-                bf16x4 ob;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ob[i] = (bf16)(OT[vb][i] * a.scale);
+                const bf16x4 ob = to_bf4(OT[vb]);
                 *(bf16x4*)((bf16*)a.o + (tok0 + t0 + cl) * a.Hv * D + h * D + 32 * wave + 16 * vb + 4 * gq) = ob;
             }
         }
@@ -422,11 +451,10 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             const int64_t jck = tend / a.ck_every;
             store_state(a.tape + ((tape_base + jck - 1) * a.Hv + h) * (int64_t)D * D, S, wave, gq, cl);
         }
-    }
-    {
-        const int lane = tid & 63;
-        if (a.s_final != nullptr) store_state(a.s_final + slab, S, wave, lane >> 4, lane & 15);
-    }
+    };
+    for (int ci = 0; ci < nfull; ++ci) chunk(ci, std::false_type{});
+    if (nfull < nchunks) chunk(nfull, std::true_type{});
+    if (a.s_final != nullptr) store_state(a.s_final + slab, S, wave, (tid & 63) >> 4, tid & 15);
 }
 
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s) {
