@@ -354,15 +354,25 @@ kda_status kda_fwd_ctx_bytes(const kda_problem* pp, size_t* bytes) {
     return KDA_OK;
 }
 
-static size_t ws_layout(const Prob& p, size_t* off_states, size_t* off_dqk, size_t* off_par) {
+// Backward workspace: the rebuild's per-chunk records (BF16 chunk-start
+// state, BF16 U, FP32 T^T / Akk^T / Aqk), then FP32 dq/dk partials when value
+// heads share a q/k head, then per-task parameter-gradient partials.
+struct WsLayout {
+    size_t s0, u, ta, dqk, par, total;
+};
+static WsLayout ws_layout(const Prob& p) {
+    WsLayout w;
+    const size_t recs = (size_t)p.total_chunks * p.Hv;
     size_t off = 0;
-    *off_states = off;
-    off = align256(off + (size_t)p.total_chunks * p.Hv * kStateElems * sizeof(float));
-    *off_dqk = off;
+    w.s0 = off;  off = align256(off + recs * kStateElems * 2);
+    w.u = off;   off = align256(off + recs * kChunk * D * 2);
+    w.ta = off;  off = align256(off + recs * 3 * kChunk * kChunk * sizeof(float));
+    w.dqk = off;
     if (p.G > 1) off = align256(off + (size_t)p.tokens * p.Hv * 2 * D * sizeof(float));
-    *off_par = off;
+    w.par = off;
     off = align256(off + (size_t)p.num_tasks * 2 * D * sizeof(float));
-    return off;
+    w.total = off;
+    return w;
 }
 
 kda_status kda_bwd_workspace_bytes(const kda_problem* pp, size_t* bytes) {
@@ -370,8 +380,7 @@ kda_status kda_bwd_workspace_bytes(const kda_problem* pp, size_t* bytes) {
     kda_status s = validate(pp, p);
     if (s != KDA_OK) return s;
     if (bytes == nullptr) return fail(KDA_ERR_NULL_ARG, "bytes is NULL");
-    size_t a, b, c;
-    *bytes = ws_layout(p, &a, &b, &c);
+    *bytes = ws_layout(p).total;
     return KDA_OK;
 }
 
@@ -454,8 +463,8 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
         return fail(KDA_ERR_NULL_ARG, "a tensor argument of kda_bwd is NULL");
     if (ctx_bytes < ctx_bytes_for(p))
         return fail(KDA_ERR_CTX_SIZE, "context has %zu bytes, needs %zu", ctx_bytes, ctx_bytes_for(p));
-    size_t off_states, off_dqk, off_par;
-    const size_t need = ws_layout(p, &off_states, &off_dqk, &off_par);
+    const WsLayout wl = ws_layout(p);
+    const size_t need = wl.total;
     if (workspace_bytes < need)
         return fail(KDA_ERR_WORKSPACE_SIZE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
     hipStream_t stream = (hipStream_t)stream_;
@@ -502,13 +511,14 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
     b.f = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, initial_state);
     b.f.tape = (float*)((char*)ctx + 256);
     char* ws = (char*)workspace;
-    b.f.chunk_states = (float*)(ws + off_states);
+    b.f.rec_s0 = (kda::bf16_t*)(ws + wl.s0);
+    b.f.rec_u = (kda::bf16_t*)(ws + wl.u);
+    b.f.rec_ta = (float*)(ws + wl.ta);
     b.d_o = d_o; b.dfinal = dfinal_state;
     b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg; b.dbeta = dbeta;
     b.dA_log = dA_log; b.ddt_bias = ddt_bias; b.dinit = dinitial_state;
-    b.chunk_states = (const float*)(ws + off_states);
-    b.dqk_part = p.G > 1 ? (float*)(ws + off_dqk) : nullptr;
-    b.dparam_part = (float*)(ws + off_par);
+    b.dqk_part = p.G > 1 ? (float*)(ws + wl.dqk) : nullptr;
+    b.dparam_part = (float*)(ws + wl.par);
     b.total_tokens = p.tokens;
 
     // segment list sits after the chunk offsets in the schedule

@@ -81,6 +81,20 @@ __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// The 16x16 identity as an MFMA operand: lane (gq, n) holds I[4gq+i][n].
+__device__ __forceinline__ bf16x4 identity_frag(int lane) {
+    const int gq = lane >> 4, cl = lane & 15;
+    f32x4 id;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) id[i] = (4 * gq + i == cl) ? 1.0f : 0.0f;
+    return to_bf4(id);
+}
+// Exact transpose of a BF16 frag through the matrix unit: if lane (gq, m)
+// holds X[m][4gq+i], the result's lane (gq, n) holds X[4gq+i][n].
+__device__ __forceinline__ f32x4 transpose_frag(bf16x4 x, bf16x4 ident) {
+    return mma16(x, ident, zero4());
+}
+
 // Sum over each row of 16 lanes, broadcast to the row, with DPP lane swaps
 // (xor 1, xor 2 inside quads, then mirrors of 8 and 16 lanes).
 __device__ __forceinline__ float row16_sum(float x) {

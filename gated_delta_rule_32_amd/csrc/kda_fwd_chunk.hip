@@ -42,15 +42,13 @@
 // sequences: final-state error ~2e-5 to 5e-5).
 #include <type_traits>
 
-#include "kda_common.hpp"
-#include "kda_kernels.h"
+#include "kda_chunk.hpp"
 
 namespace kda {
 
 namespace {
 
 constexpr int FC_THREADS = 256;
-constexpr int FS = 264;  // frag slot stride in bf16 (256 + 8 padding)
 constexpr int TBS = 20;  // row stride of the per-wave Tb scratch (16-byte rows)
 
 struct WaveScratch {         // private to one wave: no barrier between its uses
@@ -72,34 +70,10 @@ struct FwdLds {
     alignas(16) bf16 cf_ktl[8 * FS];
 };
 
-__device__ __forceinline__ int rf_off(int c, int k) {  // (token c, channel k) in an RF slot set
-    return (k >> 4) * FS + ((((k >> 2) & 3) << 4) + c) * 4 + (k & 3);
-}
-__device__ __forceinline__ int cf_off(int c, int k) {  // (token c, channel k) in a CF slot set
-    return (k >> 4) * FS + (((c >> 2) << 4) + (k & 15)) * 4 + (c & 3);
-}
-__device__ __forceinline__ bf16x4 ld4(const bf16* slot, int lane) {
-    return *(const bf16x4*)(slot + lane * 4);
-}
-
-struct RowIn {   // one token row, 8 channels (row-owner mapping)
-    bf16x8 q, k, g;
-    bf16 b;
-};
 struct ColIn {   // V for the wave's 32 columns: RF(V)[2w], RF(V)[2w+1]
     bf16x4 v0, v1;
 };
 
-// Loads are unconditional (the row is clamped into the sequence by the
-// caller): a load in a conditional block tends to be sunk next to its use.
-__device__ __forceinline__ void load_rows(RowIn& x, const FwdArgs& a, int64_t tok, int hq, int h,
-                                          int c8) {
-    const int64_t qo = tok * a.Hqk * D + hq * D + c8;
-    x.q = *(const bf16x8*)((const bf16*)a.q + qo);
-    x.k = *(const bf16x8*)((const bf16*)a.k + qo);
-    x.g = *(const bf16x8*)((const bf16*)a.g + tok * a.Hv * D + h * D + c8);
-    x.b = ((const bf16*)a.beta)[tok * a.Hv + h];
-}
 __device__ __forceinline__ void load_cols(ColIn& x, const FwdArgs& a, int64_t tok, int h,
                                           int ch0) {
     const bf16* p = (const bf16*)a.v + tok * a.Hv * D + h * D + ch0;
@@ -119,71 +93,48 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], 
         }
 }
 
-// Column-layout stores of one 4-channel group for a pair of token rows.
-// Rows c (even) and c+1 sit in lane rows 2p and 2p+1 of the wave; after one
-// lane-row swap the even row's lanes hold both rows' values for channels
-// c8+4..c8+7 and the odd row's lanes for c8..c8+3, so each lane writes four
-// (row c, row c+1) pairs as 32-bit words (the two rows are adjacent in CF).
-__device__ __forceinline__ void store_cf_pairs(bf16* slots, int r, int c8, bf16x4 lo, bf16x4 hi) {
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 ulo = __builtin_bit_cast(u32x2, lo);
-    const u32x2 uhi = __builtin_bit_cast(u32x2, hi);
-    // swap(a = hi, b = lo): lane row 2p receives row 2p+1's `hi` in the second
-    // result, lane row 2p+1 receives row 2p's `lo` in the first.
-    const auto s0 = __builtin_amdgcn_permlane16_swap(uhi[0], ulo[0], false, false);
-    const auto s1 = __builtin_amdgcn_permlane16_swap(uhi[1], ulo[1], false, false);
-    const bool even = (r & 1) == 0;
-    const u32x2 p = even ? u32x2{s0[1], s1[1]} : u32x2{s0[0], s1[0]};
-    const u32x2 m = even ? uhi : ulo;
-    // (even-row value, odd-row value) pairs: the even row's bf16 goes to the
-    // low half; byte selectors for the low / high bf16 of each source word
-    const unsigned sel_lo = even ? 0x05040100u : 0x01000504u;
-    const unsigned sel_hi = even ? 0x07060302u : 0x03020706u;
-    const int kbase = c8 + (even ? 4 : 0);
-    unsigned* dst = (unsigned*)&slots[cf_off(r & ~1, kbase)];  // channel kbase+j at +2j words
-    dst[0] = __builtin_amdgcn_perm(p[0], m[0], sel_lo);
-    dst[2] = __builtin_amdgcn_perm(p[0], m[0], sel_hi);
-    dst[4] = __builtin_amdgcn_perm(p[1], m[1], sel_lo);
-    dst[6] = __builtin_amdgcn_perm(p[1], m[1], sel_hi);
-}
-
-// Broadcast lane q of every quad to the whole quad (DPP quad_perm [q,q,q,q]);
-// q must fold to a constant.
-__device__ __forceinline__ float quad_bcast(float x, int q) {
-    const int xi = __float_as_int(x);
-    switch (q) {
-        case 0: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0x00, 0xF, 0xF, false));
-        case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0x55, 0xF, 0xF, false));
-        case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0xAA, 0xF, 0xF, false));
-        default: return __int_as_float(__builtin_amdgcn_mov_dpp(xi, 0xFF, 0xF, 0xF, false));
-    }
-}
-
-__device__ __forceinline__ void set_prio_by_remaining(int left, int total) {
-    const int p = (4 * left - 1) / total;  // 3 for the first quarter, 0 for the last
-    switch (p) {
-        case 3: __builtin_amdgcn_s_setprio(3); break;
-        case 2: __builtin_amdgcn_s_setprio(2); break;
-        case 1: __builtin_amdgcn_s_setprio(1); break;
-        default: __builtin_amdgcn_s_setprio(0); break;
-    }
-}
-
 }  // namespace
 
+// kRebuild = false: the training forward over whole tasks (o, final state,
+// tape).  kRebuild = true: the backward's state rebuild over one tape segment
+// of one task: it starts from the segment's checkpoint, writes no output, and
+// stores for every chunk the records the adjoint reads (chunk-start state, U,
+// T, Akk, Aqk).
+template <bool kRebuild>
 __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     __shared__ FwdLds sm;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
 
-    const int code = a.plan.task[blockIdx.x];
-    const int n = code / a.Hv;
-    const int h = code - n * a.Hv;
+    int n, h, seg = 0;
+    if constexpr (kRebuild) {
+        // item = segment index * Hv + h; the segment list holds (n, j) pairs
+        const int sidx = blockIdx.x / a.Hv;
+        h = blockIdx.x - sidx * a.Hv;
+        n = a.plan.task[2 * sidx];
+        seg = a.plan.task[2 * sidx + 1];
+    } else {
+        const int code = a.plan.task[blockIdx.x];
+        n = code / a.Hv;
+        h = code - n * a.Hv;
+    }
     const int hq = h / a.G;
     const int64_t tok0 = a.plan.seq_start[n];
     const int L = a.plan.seq_len[n];
     const int64_t slab = ((int64_t)n * a.Hv + h) * D * D;
     const int64_t tape_base = a.tape != nullptr ? a.plan.tape_off[n] : 0;
+    const int nchunks = (L + CH - 1) / CH;
+    const int nfull = L / CH;
+    int cb = 0, ce = nchunks;
+    const float* src = a.s0 + slab;
+    int64_t rec0 = 0;
+    if constexpr (kRebuild) {
+        const int per = a.ck_every / CH;
+        cb = seg * per;
+        ce = min(cb + per, nchunks);
+        if (seg > 0) src = a.tape + ((tape_base + seg - 1) * a.Hv + h) * (int64_t)D * D;
+        rec0 = a.plan.chunk_off[n];
+    }
 
     // state: S^T frags for kb = 0..7 and vb = 2*wave + {0, 1}
     f32x4 S[8][2];
@@ -194,8 +145,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int vcol = 16 * (2 * wave + j) + cl;
-                const float4 x =
-                    *(const float4*)(a.s0 + slab + (int64_t)vcol * D + 16 * kb + 4 * gq);
+                const float4 x = *(const float4*)(src + (int64_t)vcol * D + 16 * kb + 4 * gq);
                 S[kb][j] = f32x4{x.x, x.y, x.z, x.w};
             }
     }
@@ -210,13 +160,11 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     ColIn vcur;
     {
         const int lane = tid & 63;
-        load_rows(cur, a, tok0 + min(tid >> 4, L - 1), hq, h, (tid & 15) * 8);
-        load_cols(vcur, a, tok0 + min(lane & 15, L - 1), h, 32 * wave + 4 * (lane >> 4));
+        load_rows(cur, a, tok0 + min(cb * CH + (tid >> 4), L - 1), hq, h, (tid & 15) * 8);
+        load_cols(vcur, a, tok0 + min(cb * CH + (lane & 15), L - 1), h, 32 * wave + 4 * (lane >> 4));
     }
     __syncthreads();
 
-    const int nchunks = (L + CH - 1) / CH;
-    const int nfull = L / CH;
     // One chunk; full chunks are compiled without the tail masks.
     auto chunk = [&](const int ci, auto tail_tag) __attribute__((always_inline)) {
         constexpr bool kTail = decltype(tail_tag)::value;
@@ -237,7 +185,8 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         // waves, so without this the first workgroup on a CU races ahead and
         // the last one finishes alone; raising the priority of those with
         // more chunks left keeps co-resident tasks abreast.
-        set_prio_by_remaining(nchunks - ci, nchunks);
+        set_prio_by_remaining(ce - ci, ce - cb);
+        const int64_t rec = (rec0 + ci) * a.Hv + h;  // record index (rebuild only)
 
         // ---- A: norms, gate, beta ----
         float rq, rk;   // 1/sqrt(128)/|q| and 1/|k| (zero for rows past the end)
@@ -337,6 +286,15 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             col.z = (cl < 4 * gq + 2) ? b4.z * akk[2] : 0.f;
             col.w = (cl < 4 * gq + 3) ? b4.w * akk[3] : 0.f;
             *(float4*)&ws.nT[cl][4 * gq] = col;
+            if (kRebuild && wave == 0) {
+                // Akk^T[col][row] = Akk[row][col] for row > col
+                float4 m;
+                m.x = (cl < 4 * gq + 0) ? akk[0] : 0.f;
+                m.y = (cl < 4 * gq + 1) ? akk[1] : 0.f;
+                m.z = (cl < 4 * gq + 2) ? akk[2] : 0.f;
+                m.w = (cl < 4 * gq + 3) ? akk[3] : 0.f;
+                *(float4*)(a.rec_ta + rec * 768 + 256 + cl * 16 + 4 * gq) = m;
+            }
         }
         // Y = Kg S0^T and O^T = S0 Qg^T: independent of the substitution
         f32x4 Y[2] = {zero4(), zero4()};
@@ -344,12 +302,30 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
-            const bf16x8 q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
+            bf16x4 q0, q1;
+            if constexpr (!kRebuild) {
+                q0 = ld4(&sm.rf_qg[(2 * j) * FS], lane);
+                q1 = ld4(&sm.rf_qg[(2 * j + 1) * FS], lane);
+            }
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb) {
-                const bf16x8 s8 = cat8(to_bf4(S[2 * j][vb]), to_bf4(S[2 * j + 1][vb]));
+                const bf16x4 s0 = to_bf4(S[2 * j][vb]);
+                const bf16x4 s1 = to_bf4(S[2 * j + 1][vb]);
+                const bf16x8 s8 = cat8(s0, s1);
                 Y[vb] = mma32(kg8, s8, Y[vb]);    // lane (gq, v) holds Y[4gq+i][v]
-                OT[vb] = mma32(s8, q8, OT[vb]);   // lane (gq, c) holds O[c][v=4gq+i]
+                if constexpr (!kRebuild) {
+                    // 16x16x16 steps: this chain ends with one more below
+                    OT[vb] = mma16(s0, q0, OT[vb]);   // lane (gq, c) holds O[c][v=4gq+i]
+                    OT[vb] = mma16(s1, q1, OT[vb]);
+                } else {
+                    // chunk-start state record: frag (kb, vb) with lane (gq, k)
+                    // holding S0[16vb + 4gq + i][16kb + k]
+                    const bf16x4 ident = identity_frag(lane);
+                    const int vbg = 2 * wave + vb;
+                    bf16* dst = (bf16*)a.rec_s0 + rec * (D * D) + lane * 4;
+                    *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) = to_bf4(transpose_frag(s0, ident));
+                    *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) = to_bf4(transpose_frag(s1, ident));
+                }
             }
         }
         // T = (I + N)^-1 by right-looking substitution on all 64 lanes: lane
@@ -375,6 +351,8 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 y[2] -= nm.z * tm;
                 y[3] -= nm.w * tm;
             }
+            if (kRebuild && wave == 0)   // T^T[col][row]
+                *(float4*)(a.rec_ta + rec * 768 + col * 16 + 4 * qd) = make_float4(y[0], y[1], y[2], y[3]);
             // Tb[i][col] = T[i][col] beta_col
             const float bc = sm.beta[ci & 1][col];
 #pragma unroll
@@ -388,7 +366,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         }
         // RF16(Aqk) = frag of Aqk^T = Ki Qg^T, causal part
         bf16x4 aq;
-        {
+        if (!kRebuild || wave == 0) {
             f32x4 aqkT = zero4();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -400,6 +378,8 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) am[i] = (4 * gq + i <= cl) ? aqkT[i] : 0.f;
             aq = to_bf4(am);
+            if (kRebuild)   // Aqk[row = cl][col = 4gq + i], scale included
+                *(float4*)(a.rec_ta + rec * 768 + 512 + cl * 16 + 4 * gq) = make_float4(am[0], am[1], am[2], am[3]);
         }
         // CF(V) for the wave's columns (RF(V) times the identity, exact), then
         // U = Tb V - Tb Y
@@ -424,6 +404,12 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
         for (int vb = 0; vb < 2; ++vb) {
             split4(U[vb], uh[vb], ul[vb]);
+            if constexpr (kRebuild) {
+                // U record, RF layout: lane (gq, c) holds U[c][16vb + 4gq + i]
+                const bf16x4 ut = to_bf4(transpose_frag(to_bf4(U[vb]), identity_frag(lane)));
+                *(bf16x4*)((bf16*)a.rec_u + rec * (CH * D) + ((2 * wave + vb) * 64 + lane) * 4) = ut;
+                continue;
+            }
             OT[vb] = mma16(uh[vb], aq, OT[vb]);
             // lane (gq, c) holds O[c][32w + 16vb + 4gq + i]
             if (cl < nv) {
@@ -431,35 +417,47 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 *(bf16x4*)((bf16*)a.o + (tok0 + t0 + cl) * a.Hv * D + h * D + 32 * wave + 16 * vb + 4 * gq) = ob;
             }
         }
+        // (one accumulation chain keeps one MFMA shape: a 16x16x16 that reads
+        // the accumulator of a 16x16x32 issued just before it has been seen
+        // to miss that product)
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
             const bf16x4 th = ld4(&sm.cf_kth[kb * FS], lane);
             const bf16x4 tl = ld4(&sm.cf_ktl[kb * FS], lane);
-            const bf16x8 thh = cat8(th, th);
             const float4 gd = *(const float4*)&sm.gamc[16 * kb + 4 * gq];
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb) {
                 f32x4 s = S[kb][vb];
                 s[0] *= gd.x; s[1] *= gd.y; s[2] *= gd.z; s[3] *= gd.w;
-                s = mma32(thh, cat8(uh[vb], ul[vb]), s);
+                s = mma16(th, uh[vb], s);
+                s = mma16(th, ul[vb], s);
                 s = mma16(tl, uh[vb], s);
                 S[kb][vb] = s;
             }
         }
         const int tend = t0 + nv;
-        if (a.tape != nullptr && tend < L && (tend % a.ck_every) == 0) {
+        if (!kRebuild && a.tape != nullptr && tend < L && (tend % a.ck_every) == 0) {
             const int64_t jck = tend / a.ck_every;
             store_state(a.tape + ((tape_base + jck - 1) * a.Hv + h) * (int64_t)D * D, S, wave, gq, cl);
         }
     };
-    for (int ci = 0; ci < nfull; ++ci) chunk(ci, std::false_type{});
-    if (nfull < nchunks) chunk(nfull, std::true_type{});
-    if (a.s_final != nullptr) store_state(a.s_final + slab, S, wave, (tid & 63) >> 4, tid & 15);
+    const int cfull = min(ce, nfull);
+    for (int ci = cb; ci < cfull; ++ci) chunk(ci, std::false_type{});
+    if (nfull < ce) chunk(nfull, std::true_type{});
+    if (!kRebuild && a.s_final != nullptr)
+        store_state(a.s_final + slab, S, wave, (tid & 63) >> 4, tid & 15);
 }
 
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s) {
     if (a.num_tasks == 0) return hipSuccess;
-    hipLaunchKernelGGL(fwd_chunk_kernel, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0, s, a);
+    hipLaunchKernelGGL(fwd_chunk_kernel<false>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0, s, a);
+    return hipGetLastError();
+}
+
+// One workgroup per (tape segment, value head): num_items = segments * Hv.
+hipError_t launch_state_rebuild(const FwdArgs& a, int64_t num_items, hipStream_t s) {
+    if (num_items == 0) return hipSuccess;
+    hipLaunchKernelGGL(fwd_chunk_kernel<true>, dim3((unsigned)num_items), dim3(FC_THREADS), 0, s, a);
     return hipGetLastError();
 }
 

@@ -6,6 +6,8 @@
 
 namespace kda {
 
+typedef unsigned short bf16_t;  // BF16 bits in memory
+
 // Device-side schedule built on the host from the sequence lengths.  Task i
 // (0 <= i < num_tasks, longest sequence first) is (n, h) = (task[i] / Hv,
 // task[i] % Hv).  Sequence n occupies flattened tokens [seq_start[n],
@@ -32,7 +34,11 @@ struct FwdArgs {
     void* o;
     float* s_final;         // [N][Hv][128][128]; may be null (state rebuild)
     float* tape;            // [ck][Hv][128][128]; may be null
-    float* chunk_states;    // [chunks][Hv][128][128] state at every chunk start; may be null
+    // Per-chunk records written by the state rebuild and read by the adjoint,
+    // indexed by rec = (chunk_off[n] + chunk) * Hv + h (layouts: kda_bwd.hip).
+    bf16_t* rec_s0;         // [rec][8 kb][8 vb][64][4] chunk-start state, BF16
+    bf16_t* rec_u;          // [rec][8 vb][64][4] U, BF16
+    float* rec_ta;          // [rec][3][16][16] T^T, Akk^T, scale*Aqk
     DevPlan plan;
     int Hqk, Hv, G;
     int num_tasks;
@@ -49,7 +55,6 @@ struct BwdArgs {
     const float* dfinal;
     void* dq; void* dk; void* dv; void* dg; void* dbeta;
     float* dA_log; float* ddt_bias; float* dinit;
-    const float* chunk_states;  // rebuilt chunk-start states
     float* dqk_part;        // [tokens][Hv][2][128] FP32 partial dq,dk when G > 1; else null
     float* dparam_part;     // [tasks][2][128]: per-task ddt_bias and dA_log partial sums
     int64_t total_tokens;

@@ -7,5 +7,5 @@ from .kda_oracle import (  # noqa: F401
     EPS, LOWER_BOUND, SCALE, prologue, recurrence, forward_task, backward_task,
     recurrence_backward, prologue_backward, chunk_quantities, chunk_recurrence,
     chunk_forward_task, chunk_recurrence_backward, chunk_backward_task,
-    forward, backward, task_list, default_workers,
+    forward, backward, forward_tasks, backward_tasks, task_list, default_workers,
 )

@@ -420,6 +420,40 @@ def _map(fn, jobs, workers):
         return pool.map(fn, jobs, chunksize=1)
 
 
+def _task_jobs(tl, q, k, v, g, beta, A_log, dt_bias, initial_state, do=None, dfinal_state=None):
+    # each job carries FP64 copies of its own slices only
+    jobs = []
+    for (n, h, hq, b, t0, L) in tl:
+        s = slice(t0, t0 + L)
+        job = (n, h, _np64(q[b, s, hq]), _np64(k[b, s, hq]), _np64(v[b, s, h]), _np64(g[b, s, h]),
+               _np64(beta[b, s, h]), float(A_log[h]), _np64(dt_bias[h]), _np64(initial_state[n, h]))
+        if do is not None:
+            job = job + (_np64(do[b, s, h]), _np64(dfinal_state[n, h]))
+        jobs.append(job)
+    return jobs
+
+
+def forward_tasks(q, k, v, g, beta, A_log, dt_bias, initial_state, lengths, packed, tasks,
+                  workers=None):
+    """Forward of the given (n, h) tasks: {(n, h): (o [L, d], S_L [d, d])} in FP64.
+    Arrays follow the training API's tensor contract (see `forward`)."""
+    Hqk, Hv = q.shape[2], v.shape[2]
+    tl = task_list(lengths, packed, Hqk, Hv, tasks)
+    jobs = _task_jobs(tl, q, k, v, g, beta, A_log, dt_bias, initial_state)
+    return {(n, h): (o, S) for n, h, o, S in _map(_fwd_job, jobs, workers)}
+
+
+def backward_tasks(q, k, v, g, beta, A_log, dt_bias, initial_state, do, dfinal_state,
+                   lengths, packed, tasks, workers=None):
+    """Backward of the given (n, h) tasks: {(n, h): (dq, dk, dv, dg, dbeta,
+    dA_log_h, ddt_bias_h, dS0)} in FP64, where dq and dk are this value head's
+    contribution to its q/k head and dA_log_h, ddt_bias_h this task's share."""
+    Hqk, Hv = q.shape[2], v.shape[2]
+    tl = task_list(lengths, packed, Hqk, Hv, tasks)
+    jobs = _task_jobs(tl, q, k, v, g, beta, A_log, dt_bias, initial_state, do, dfinal_state)
+    return {(r[0], r[1]): r[2:] for r in _map(_bwd_job, jobs, workers)}
+
+
 def forward(q, k, v, g, beta, A_log, dt_bias, initial_state, lengths, packed,
             tasks=None, workers=None):
     """Whole-problem forward. Arrays follow the training API's tensor contract
@@ -429,20 +463,14 @@ def forward(q, k, v, g, beta, A_log, dt_bias, initial_state, lengths, packed,
     Returns (o [B,T,Hv,d], final_state [N,Hv,d,d]) in FP64. With `tasks`
     (a list of (n, h)) only those tasks are computed and the rest of the
     outputs is NaN."""
-    q, k, v, g, beta = map(_np64, (q, k, v, g, beta))
-    A_log, dt_bias, S0 = map(_np64, (A_log, dt_bias, initial_state))
     Hqk, Hv = q.shape[2], v.shape[2]
     tl = task_list(lengths, packed, Hqk, Hv, tasks)
-    jobs = []
+    res = forward_tasks(q, k, v, g, beta, A_log, dt_bias, initial_state, lengths, packed,
+                        [(n, h) for (n, h, *_r) in tl], workers)
+    o = np.full(tuple(v.shape), np.nan)
+    fs = np.full(tuple(initial_state.shape), np.nan)
     for (n, h, hq, b, t0, L) in tl:
-        s = slice(t0, t0 + L)
-        jobs.append((n, h, q[b, s, hq], k[b, s, hq], v[b, s, h], g[b, s, h], beta[b, s, h],
-                     float(A_log[h]), dt_bias[h], S0[n, h]))
-    o = np.full(v.shape, np.nan)
-    fs = np.full(S0.shape, np.nan)
-    sl = {n: (b, t0, L) for (n, _, _, b, t0, L) in tl}
-    for n, h, on, Sn in _map(_fwd_job, jobs, workers):
-        b, t0, L = sl[n]
+        on, Sn = res[(n, h)]
         o[b, t0:t0 + L, h] = on
         fs[n, h] = Sn
     return o, fs
@@ -455,31 +483,21 @@ def backward(q, k, v, g, beta, A_log, dt_bias, initial_state, do, dfinal_state,
     that share a q/k head; dA_log and ddt_bias sum over every sequence and
     token. With `tasks`, only those tasks contribute (outputs of other tasks
     are NaN; dq/dk/dA_log/ddt_bias hold partial sums)."""
-    q, k, v, g, beta = map(_np64, (q, k, v, g, beta))
-    A_log, dt_bias, S0 = map(_np64, (A_log, dt_bias, initial_state))
-    do, dfs = _np64(do), _np64(dfinal_state)
     Hqk, Hv = q.shape[2], v.shape[2]
     tl = task_list(lengths, packed, Hqk, Hv, tasks)
-    jobs = []
+    res = backward_tasks(q, k, v, g, beta, A_log, dt_bias, initial_state, do, dfinal_state,
+                         lengths, packed, [(n, h) for (n, h, *_r) in tl], workers)
+    fill = np.nan if tasks is not None else 0.0
+    dq = np.zeros(tuple(q.shape))
+    dk = np.zeros(tuple(k.shape))
+    dv = np.full(tuple(v.shape), fill)
+    dg = np.full(tuple(g.shape), fill)
+    dbeta = np.full(tuple(beta.shape), fill)
+    dA = np.zeros(tuple(A_log.shape))
+    ddt = np.zeros(tuple(dt_bias.shape))
+    dS0 = np.full(tuple(initial_state.shape), fill)
     for (n, h, hq, b, t0, L) in tl:
-        s = slice(t0, t0 + L)
-        jobs.append((n, h, q[b, s, hq], k[b, s, hq], v[b, s, h], g[b, s, h], beta[b, s, h],
-                     float(A_log[h]), dt_bias[h], S0[n, h], do[b, s, h], dfs[n, h]))
-    partial = tasks is not None
-    fill = np.nan if partial else 0.0
-    dq = np.zeros(q.shape)
-    dk = np.zeros(k.shape)
-    dv = np.full(v.shape, fill)
-    dg = np.full(g.shape, fill)
-    dbeta = np.full(beta.shape, fill)
-    dA = np.zeros(A_log.shape)
-    ddt = np.zeros(dt_bias.shape)
-    dS0 = np.full(S0.shape, fill)
-    info = {n: (hq, b, t0, L) for (n, h, hq, b, t0, L) in tl}
-    hqs = {h: hq for (n, h, hq, b, t0, L) in tl}
-    for (n, h, dqt, dkt, dvt, dgt, dbt, dAt, ddtt, dS0t) in _map(_bwd_job, jobs, workers):
-        hq, b, t0, L = info[n]
-        hq = hqs[h]
+        dqt, dkt, dvt, dgt, dbt, dAt, ddtt, dS0t = res[(n, h)]
         s = slice(t0, t0 + L)
         dq[b, s, hq] += dqt
         dk[b, s, hq] += dkt
@@ -492,8 +510,11 @@ def backward(q, k, v, g, beta, A_log, dt_bias, initial_state, do, dfinal_state,
     return dq, dk, dv, dg, dbeta, dA, ddt, dS0
 
 
-def default_workers():
+def default_workers(cap=16):
+    """Worker processes for the task pool: the CPUs this process may use, at
+    most `cap`."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    return max(1, min(n, cap))

@@ -42,6 +42,12 @@ class Problem:
     zero_state: bool = False
     name: str = "custom"
 
+    def __post_init__(self):
+        if not self.lengths or min(self.lengths) < 1:
+            raise ValueError("every sequence needs at least one token")
+        if not self.packed and len(set(self.lengths)) != 1:
+            raise ValueError("the fixed layout has one length T for every sequence")
+
     @property
     def N(self) -> int:
         return len(self.lengths)
