@@ -24,6 +24,42 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "KDA fwd token-heads/sec (packed 8x1024, 96 heads, 1 GPU); % roofline; bwd time"
+# HBM traffic of the chunked forward from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes, scaled by a copy kernel of known size; valid only for the kernel
+# sources it was taken with (their SHA-256 is recorded beside the figures).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_chunk_kernel_packed_8x1024_h96_traffic.txt")
+FWD_SOURCES = ["gated_delta_rule_32_amd/csrc/kda_fwd_chunk.hip",
+               "gated_delta_rule_32_amd/csrc/kda_chunk.hpp",
+               "gated_delta_rule_32_amd/csrc/kda_common.hpp",
+               "gated_delta_rule_32_amd/csrc/kda_kernels.h"]
+
+
+def fwd_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in FWD_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Measured HBM bytes per launch of the chunked forward, or None when no
+    measurement exists for the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != fwd_source_sha():
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic_fwd_bytes(problem) -> int:
@@ -33,6 +69,28 @@ def algorithmic_fwd_bytes(problem) -> int:
     G = problem.Hv // problem.Hqk
     per_tok_head = 2 * 128 * 2 / G + 128 * 2 * 3 + 2
     return int(toks * problem.Hv * per_tok_head + problem.N * problem.Hv * 2 * 128 * 128 * 4)
+
+
+def algorithmic_bwd_bytes(problem) -> int:
+    """Bytes the backward must move at least: q, k (shared by G heads), v, g,
+    beta, do read and dq, dk, dv, dg, dbeta written per token-head; the
+    initial state and dfinal_state read and dinitial_state written per task."""
+    toks = sum(problem.lengths)
+    G = problem.Hv // problem.Hqk
+    per_tok_head = 4 * 128 * 2 / G + 128 * 2 * 5 + 2 * 2
+    return int(toks * problem.Hv * per_tok_head + problem.N * problem.Hv * 3 * 128 * 128 * 4)
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """Plain device-to-device copies of a known size, to scale the HBM byte
+    counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_copy": nbytes, "copies": reps}), flush=True)
 
 
 def cpu_baseline(inp, max_seconds: float = 30.0):
@@ -70,11 +128,17 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--route", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain copies of 1 GiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
     import workloads
@@ -137,12 +201,13 @@ def main():
 
     algo = algorithmic_fwd_bytes(p)
     achieved = algo / (fwd_mean * 1e-3) / 1e9
+    traffic = recorded_traffic() if (route == 1 and p.name == "packed") else None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": "fwd_chunk_kernel" if route == 1 else "fwd_rowsplit_kernel",
             "algorithmic_bytes_per_launch": algo, "avg_launch_ms": round(fwd_mean, 4)}
     out = {
-        "metric": "KDA fwd token-heads/sec (packed 8x1024, 96 heads, 1 GPU)",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "token-heads/s",
         "n_gpus": 1,
@@ -164,6 +229,15 @@ def main():
                    "tape_interval": 256, "step": "fwd+bwd" if do_bwd else "fwd"},
         "roofline": roof,
     }
+    if do_bwd:
+        bwd_mean = sum(bwd_ms) / len(bwd_ms)
+        ab = algorithmic_bwd_bytes(p)
+        out["bwd"] = {"ms_mean": round(bwd_mean, 4),
+                      "algorithmic_bytes": ab,
+                      "achieved_GBs": round(ab / (bwd_mean * 1e-3) / 1e9, 1),
+                      "frac_of_hbm_peak": round(ab / (bwd_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "kernels": ["fwd_chunk_kernel<rebuild>", "bwd_chunk_kernel",
+                                  "bwd_param_reduce_kernel", "bwd_dqk_reduce_kernel"]}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp_cpu)
     print(json.dumps(out), flush=True)
