@@ -302,22 +302,13 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
-            bf16x4 q0, q1;
-            if constexpr (!kRebuild) {
-                q0 = ld4(&sm.rf_qg[(2 * j) * FS], lane);
-                q1 = ld4(&sm.rf_qg[(2 * j + 1) * FS], lane);
-            }
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb) {
                 const bf16x4 s0 = to_bf4(S[2 * j][vb]);
                 const bf16x4 s1 = to_bf4(S[2 * j + 1][vb]);
                 const bf16x8 s8 = cat8(s0, s1);
                 Y[vb] = mma32(kg8, s8, Y[vb]);    // lane (gq, v) holds Y[4gq+i][v]
-                if constexpr (!kRebuild) {
-                    // 16x16x16 steps: this chain ends with one more below
-                    OT[vb] = mma16(s0, q0, OT[vb]);   // lane (gq, c) holds O[c][v=4gq+i]
-                    OT[vb] = mma16(s1, q1, OT[vb]);
-                } else {
+                if constexpr (kRebuild) {
                     // chunk-start state record: frag (kb, vb) with lane (gq, k)
                     // holding S0[16vb + 4gq + i][16kb + k]
                     const bf16x4 ident = identity_frag(lane);
@@ -400,7 +391,21 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         }
         load_cols(vcur, a, tok0 + min(t0 + CH + cl, L - 1), h, 32 * wave + 4 * gq);
         // O^T += U^T Aqk^T, store; then S update
+        // O^T = S0 Qg^T, formed here rather than beside Y: Y feeds the
+        // substitution's critical path, O^T only the store at the end
+        if constexpr (!kRebuild) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) {
+                    const bf16x8 s8 = cat8(to_bf4(S[2 * j][vb]), to_bf4(S[2 * j + 1][vb]));
+                    OT[vb] = mma32(s8, q8, OT[vb]);   // lane (gq, c) holds O[c][v=4gq+i]
+                }
+            }
+        }
         bf16x4 uh[2], ul[2];
+        const bf16x4 zb = to_bf4(zero4());
 #pragma unroll
         for (int vb = 0; vb < 2; ++vb) {
             split4(U[vb], uh[vb], ul[vb]);
@@ -410,7 +415,8 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 *(bf16x4*)((bf16*)a.rec_u + rec * (CH * D) + ((2 * wave + vb) * 64 + lane) * 4) = ut;
                 continue;
             }
-            OT[vb] = mma16(uh[vb], aq, OT[vb]);
+            // the chain's last step is a 16x16x32 as well (upper half zero)
+            OT[vb] = mma32(cat8(uh[vb], zb), cat8(aq, zb), OT[vb]);
             // lane (gq, c) holds O[c][32w + 16vb + 4gq + i]
             if (cl < nv) {
                 const bf16x4 ob = to_bf4(OT[vb]);
