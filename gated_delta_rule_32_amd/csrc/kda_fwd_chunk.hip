@@ -51,7 +51,7 @@ namespace {
 constexpr int FC_THREADS = 256;
 constexpr int TBS = 20;  // row stride of the per-wave Tb scratch (16-byte rows)
 
-struct WaveScratch {         // private to one wave: no barrier between its uses
+struct SolveScratch {        // used by wave 0 only: no barrier between its uses
     alignas(16) float nT[CH][CH];   // nT[m][i] = beta_i Akk[i][m] for i > m, else 0
     alignas(16) float tb[CH][TBS];  // Tb[i][j]
 };
@@ -62,7 +62,9 @@ struct FwdLds {
     alignas(16) float dtz[D];       // dt_bias * exp(A_log) * log2(e)
     alignas(16) float beta[2][CH];  // double-buffered: a wave may start the next
                                     // chunk while another still solves with this one's
-    WaveScratch pw[4];
+    SolveScratch sv;
+    alignas(16) bf16 sh_tb[2][256]; // RF16(Tb) hi / lo frags, written by wave 0
+    alignas(16) bf16 sh_aq[256];    // RF16(Aqk) frag, written by wave 1
     alignas(16) bf16 rf_qg[8 * FS];
     alignas(16) bf16 rf_kg[8 * FS];
     alignas(16) bf16 rf_ki[8 * FS];
@@ -269,9 +271,10 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         load_rows(cur, a, tok0 + min(t0 + CH + r, L - 1), hq, h, c8);
         __syncthreads();
 
-        // ---- D: per wave.  N = diag(beta) Akk into the wave's scratch ----
-        WaveScratch& ws = sm.pw[wave];
-        {
+        // ---- D1: the chunk's 16x16 algebra once (wave 0: Akk and the
+        // substitution; wave 1: Aqk), Y and O^T on every wave ----
+        if (wave == 0) {
+            SolveScratch& ws = sm.sv;
             f32x4 akk = zero4();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             col.z = (cl < 4 * gq + 2) ? b4.z * akk[2] : 0.f;
             col.w = (cl < 4 * gq + 3) ? b4.w * akk[3] : 0.f;
             *(float4*)&ws.nT[cl][4 * gq] = col;
-            if (kRebuild && wave == 0) {
+            if (kRebuild) {
                 // Akk^T[col][row] = Akk[row][col] for row > col
                 float4 m;
                 m.x = (cl < 4 * gq + 0) ? akk[0] : 0.f;
@@ -295,42 +298,17 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 m.w = (cl < 4 * gq + 3) ? akk[3] : 0.f;
                 *(float4*)(a.rec_ta + rec * 768 + 256 + cl * 16 + 4 * gq) = m;
             }
-        }
-        // Y = Kg S0^T and O^T = S0 Qg^T: independent of the substitution
-        f32x4 Y[2] = {zero4(), zero4()};
-        f32x4 OT[2] = {zero4(), zero4()};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
-#pragma unroll
-            for (int vb = 0; vb < 2; ++vb) {
-                const bf16x4 s0 = to_bf4(S[2 * j][vb]);
-                const bf16x4 s1 = to_bf4(S[2 * j + 1][vb]);
-                const bf16x8 s8 = cat8(s0, s1);
-                Y[vb] = mma32(kg8, s8, Y[vb]);    // lane (gq, v) holds Y[4gq+i][v]
-                if constexpr (kRebuild) {
-                    // chunk-start state record: frag (kb, vb) with lane (gq, k)
-                    // holding S0[16vb + 4gq + i][16kb + k]
-                    const bf16x4 ident = identity_frag(lane);
-                    const int vbg = 2 * wave + vb;
-                    bf16* dst = (bf16*)a.rec_s0 + rec * (D * D) + lane * 4;
-                    *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) = to_bf4(transpose_frag(s0, ident));
-                    *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) = to_bf4(transpose_frag(s1, ident));
-                }
-            }
-        }
-        // T = (I + N)^-1 by right-looking substitution on all 64 lanes: lane
-        // (col = lane/4, q = lane%4) keeps rows 4q..4q+3 of column col; N is
-        // zero on and above the diagonal, so no masking is needed.
-        {
-            // y[j] (row 4q+j of column col) starts at [row == col] and loses
-            // N[row][m] t[m] at every step m; row m is final when step m
-            // begins, so t[m] = y of the quad lane that holds row m.
-            const int col = lane >> 2;
+            // T = (I + N)^-1 by right-looking substitution on all 64 lanes:
+            // lane (col = lane/4, q = lane%4) keeps rows 4q..4q+3 of column
+            // col; N is zero on and above the diagonal, so no masking is
+            // needed.  y[j] (row 4q+j of column col) starts at [row == col]
+            // and loses N[row][m] t[m] at every step m; row m is final when
+            // step m begins, so t[m] = y of the quad lane that holds row m.
+            const int colx = lane >> 2;
             const int qd = lane & 3;
             float y[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) y[j] = (4 * qd + j == col) ? 1.0f : 0.0f;
+            for (int j = 0; j < 4; ++j) y[j] = (4 * qd + j == colx) ? 1.0f : 0.0f;
             float4 nxt = *(const float4*)&ws.nT[0][4 * qd];
 #pragma unroll
             for (int m = 0; m < CH; ++m) {
@@ -342,22 +320,20 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 y[2] -= nm.z * tm;
                 y[3] -= nm.w * tm;
             }
-            if (kRebuild && wave == 0)   // T^T[col][row]
-                *(float4*)(a.rec_ta + rec * 768 + col * 16 + 4 * qd) = make_float4(y[0], y[1], y[2], y[3]);
+            if (kRebuild)   // T^T[col][row]
+                *(float4*)(a.rec_ta + rec * 768 + colx * 16 + 4 * qd) = make_float4(y[0], y[1], y[2], y[3]);
             // Tb[i][col] = T[i][col] beta_col
-            const float bc = sm.beta[ci & 1][col];
+            const float bc = sm.beta[ci & 1][colx];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ws.tb[4 * qd + j][col] = y[j] * bc;
-        }
-        // RF16(Tb) as a hi/lo pair: lane (gq, c) holds Tb[c][4gq+i]
-        bf16x4 tbh, tbl;
-        {
+            for (int j = 0; j < 4; ++j) ws.tb[4 * qd + j][colx] = y[j] * bc;
+            // RF16(Tb) as a hi/lo pair: lane (gq, c) holds Tb[c][4gq+i]
             const float4 t4 = *(const float4*)&ws.tb[cl][4 * gq];
-            split4(f32x4{t4.x, t4.y, t4.z, t4.w}, tbh, tbl);
-        }
-        // RF16(Aqk) = frag of Aqk^T = Ki Qg^T, causal part
-        bf16x4 aq;
-        if (!kRebuild || wave == 0) {
+            bf16x4 th4, tl4;
+            split4(f32x4{t4.x, t4.y, t4.z, t4.w}, th4, tl4);
+            *(bf16x4*)&sm.sh_tb[0][lane * 4] = th4;
+            *(bf16x4*)&sm.sh_tb[1][lane * 4] = tl4;
+        } else if (wave == 1) {
+            // RF16(Aqk) = frag of Aqk^T = Ki Qg^T, causal part
             f32x4 aqkT = zero4();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -368,10 +344,51 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             f32x4 am;
 #pragma unroll
             for (int i = 0; i < 4; ++i) am[i] = (4 * gq + i <= cl) ? aqkT[i] : 0.f;
-            aq = to_bf4(am);
-            if (kRebuild)   // Aqk[row = cl][col = 4gq + i], scale included
+            if constexpr (kRebuild)   // Aqk[row = cl][col = 4gq + i], scale included
                 *(float4*)(a.rec_ta + rec * 768 + 512 + cl * 16 + 4 * gq) = make_float4(am[0], am[1], am[2], am[3]);
+            else
+                *(bf16x4*)&sm.sh_aq[lane * 4] = to_bf4(am);
         }
+        // Y = Kg S0^T and O^T = S0 Qg^T (S0 converted once for both)
+        f32x4 Y[2] = {zero4(), zero4()};
+        f32x4 OT[2] = {zero4(), zero4()};
+        {
+            bf16x8 sb[4][2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) {
+                    const bf16x4 s0 = to_bf4(S[2 * j][vb]);
+                    const bf16x4 s1 = to_bf4(S[2 * j + 1][vb]);
+                    sb[j][vb] = cat8(s0, s1);
+                    Y[vb] = mma32(kg8, sb[j][vb], Y[vb]);    // lane (gq, v) holds Y[4gq+i][v]
+                    if constexpr (kRebuild) {
+                        // chunk-start state record: frag (kb, vb) with lane (gq, k)
+                        // holding S0[16vb + 4gq + i][16kb + k]
+                        const bf16x4 ident = identity_frag(lane);
+                        const int vbg = 2 * wave + vb;
+                        bf16* dst = (bf16*)a.rec_s0 + rec * (D * D) + lane * 4;
+                        *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) = to_bf4(transpose_frag(s0, ident));
+                        *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) = to_bf4(transpose_frag(s1, ident));
+                    }
+                }
+            }
+            if constexpr (!kRebuild) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
+#pragma unroll
+                    for (int vb = 0; vb < 2; ++vb) OT[vb] = mma32(sb[j][vb], q8, OT[vb]);   // lane (gq, c): O[c][v=4gq+i]
+                }
+            }
+        }
+        __syncthreads();
+        // ---- D2 (per wave): U, output, state update ----
+        const bf16x4 tbh = ld4(&sm.sh_tb[0][0], lane);
+        const bf16x4 tbl = ld4(&sm.sh_tb[1][0], lane);
+        bf16x4 aq;
+        if constexpr (!kRebuild) aq = ld4(&sm.sh_aq[0], lane);
         // CF(V) for the wave's columns (RF(V) times the identity, exact), then
         // U = Tb V - Tb Y
         f32x4 U[2];
@@ -391,19 +408,6 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         }
         load_cols(vcur, a, tok0 + min(t0 + CH + cl, L - 1), h, 32 * wave + 4 * gq);
         // O^T += U^T Aqk^T, store; then S update
-        // O^T = S0 Qg^T, formed here rather than beside Y: Y feeds the
-        // substitution's critical path, O^T only the store at the end
-        if constexpr (!kRebuild) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
-#pragma unroll
-                for (int vb = 0; vb < 2; ++vb) {
-                    const bf16x8 s8 = cat8(to_bf4(S[2 * j][vb]), to_bf4(S[2 * j + 1][vb]));
-                    OT[vb] = mma32(s8, q8, OT[vb]);   // lane (gq, c) holds O[c][v=4gq+i]
-                }
-            }
-        }
         bf16x4 uh[2], ul[2];
         const bf16x4 zb = to_bf4(zero4());
 #pragma unroll
