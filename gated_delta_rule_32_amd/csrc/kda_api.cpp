@@ -132,6 +132,11 @@ kda_status validate(const kda_problem* p, Prob& out) {
         out.total_segs += (L + ck - 1) / ck;
         out.total_chunks += (L + kChunk - 1) / kChunk;
     }
+    // kernels address a sequence's rows with 32-bit element offsets
+    for (int64_t L : out.len)
+        if (L * (int64_t)p->Hv * D >= ((int64_t)1 << 31))
+            return fail(KDA_ERR_SHAPE, "a sequence of %lld tokens x %d heads x 128 exceeds 2^31 elements",
+                        (long long)L, p->Hv);
     out.route = p->route == 0 ? auto_route(out) : p->route;
     return KDA_OK;
 }

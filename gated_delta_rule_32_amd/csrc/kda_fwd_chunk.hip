@@ -76,11 +76,30 @@ struct ColIn {   // V for the wave's 32 columns: RF(V)[2w], RF(V)[2w+1]
     bf16x4 v0, v1;
 };
 
-__device__ __forceinline__ void load_cols(ColIn& x, const FwdArgs& a, int64_t tok, int h,
-                                          int ch0) {
-    const bf16* p = (const bf16*)a.v + tok * a.Hv * D + h * D + ch0;
-    x.v0 = *(const bf16x4*)p;
-    x.v1 = *(const bf16x4*)(p + 16);
+// Per-task base pointers (uniform, so they live in scalar registers) and
+// element strides; a token row inside the sequence is then a 32-bit offset
+// (the host rejects sequences whose span exceeds 2^31 elements).
+struct SeqPtrs {
+    const bf16* q;   // q[tok0][hq][0]; k likewise
+    const bf16* k;
+    const bf16* g;   // g[tok0][h][0]; v and o likewise
+    const bf16* v;
+    bf16* o;
+    const bf16* beta;  // beta[tok0][h]
+    unsigned sq, sv, sb;  // per-token strides: Hqk*128, Hv*128, Hv
+};
+
+__device__ __forceinline__ void load_rows_s(RowIn& x, const SeqPtrs& p, unsigned t, unsigned c8) {
+    const unsigned oq = __umul24(t, p.sq) + c8;
+    x.q = *(const bf16x8*)(p.q + oq);
+    x.k = *(const bf16x8*)(p.k + oq);
+    x.g = *(const bf16x8*)(p.g + __umul24(t, p.sv) + c8);
+    x.b = p.beta[__umul24(t, p.sb)];
+}
+__device__ __forceinline__ void load_cols_s(ColIn& x, const SeqPtrs& p, unsigned t, unsigned ch0) {
+    const bf16* q = p.v + __umul24(t, p.sv) + ch0;
+    x.v0 = *(const bf16x4*)q;
+    x.v1 = *(const bf16x4*)(q + 16);
 }
 
 __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], int wave, int gq,
@@ -158,12 +177,23 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     const float zs = eA * LOG2E;
     if (tid < D) sm.dtz[tid] = a.dt_bias[h * D + tid] * zs;
 
+    SeqPtrs sp;
+    sp.q = (const bf16*)a.q + (tok0 * a.Hqk + hq) * D;
+    sp.k = (const bf16*)a.k + (tok0 * a.Hqk + hq) * D;
+    sp.g = (const bf16*)a.g + (tok0 * a.Hv + h) * D;
+    sp.v = (const bf16*)a.v + (tok0 * a.Hv + h) * D;
+    sp.o = (bf16*)a.o + (tok0 * a.Hv + h) * D;
+    sp.beta = (const bf16*)a.beta + tok0 * a.Hv + h;
+    sp.sq = (unsigned)(a.Hqk * D);
+    sp.sv = (unsigned)(a.Hv * D);
+    sp.sb = (unsigned)a.Hv;
+
     RowIn cur;
     ColIn vcur;
     {
         const int lane = tid & 63;
-        load_rows(cur, a, tok0 + min(cb * CH + (tid >> 4), L - 1), hq, h, (tid & 15) * 8);
-        load_cols(vcur, a, tok0 + min(cb * CH + (lane & 15), L - 1), h, 32 * wave + 4 * (lane >> 4));
+        load_rows_s(cur, sp, min(cb * CH + (tid >> 4), L - 1), (tid & 15) * 8);
+        load_cols_s(vcur, sp, min(cb * CH + (lane & 15), L - 1), 32 * wave + 4 * (lane >> 4));
     }
     __syncthreads();
 
@@ -264,11 +294,19 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 *(bf16x4*)&sm.rf_kg[orf + 64 * s] = kg4[s];
                 *(bf16x4*)&sm.rf_ki[orf + 64 * s] = ki4[s];
             }
-            store_cf_pairs(sm.cf_kth, r, c8, th4[0], th4[1]);
-            store_cf_pairs(sm.cf_ktl, r, c8, tl4[0], tl4[1]);
+            // CF(Kt) hi / lo: channel c8 + j of row r sits 4j elements after
+            // channel c8 (the 8 channels share one 16-channel block)
+            const int ocf = cf_off(r, c8);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sm.cf_kth[ocf + 4 * j] = th4[0][j];
+                sm.cf_kth[ocf + 4 * (j + 4)] = th4[1][j];
+                sm.cf_ktl[ocf + 4 * j] = tl4[0][j];
+                sm.cf_ktl[ocf + 4 * (j + 4)] = tl4[1][j];
+            }
         }
         // the row inputs are dead: fetch the next chunk's into the same registers
-        load_rows(cur, a, tok0 + min(t0 + CH + r, L - 1), hq, h, c8);
+        load_rows_s(cur, sp, min(t0 + CH + r, L - 1), c8);
         __syncthreads();
 
         // ---- D1: the chunk's 16x16 algebra once (wave 0: Akk and the
@@ -406,7 +444,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             U[1] = mma16(tbl, cfv1, U[1]);
             U[1] = mma16(tbh, to_bf4(-Y[1]), U[1]);
         }
-        load_cols(vcur, a, tok0 + min(t0 + CH + cl, L - 1), h, 32 * wave + 4 * gq);
+        load_cols_s(vcur, sp, min(t0 + CH + cl, L - 1), 32 * wave + 4 * gq);
         // O^T += U^T Aqk^T, store; then S update
         bf16x4 uh[2], ul[2];
         const bf16x4 zb = to_bf4(zero4());
@@ -424,7 +462,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             // lane (gq, c) holds O[c][32w + 16vb + 4gq + i]
             if (cl < nv) {
                 const bf16x4 ob = to_bf4(OT[vb]);
-                *(bf16x4*)((bf16*)a.o + (tok0 + t0 + cl) * a.Hv * D + h * D + 32 * wave + 16 * vb + 4 * gq) = ob;
+                *(bf16x4*)(sp.o + __umul24((unsigned)(t0 + cl), sp.sv) + 32 * wave + 16 * vb + 4 * gq) = ob;
             }
         }
         // (one accumulation chain keeps one MFMA shape: a 16x16x16 that reads
