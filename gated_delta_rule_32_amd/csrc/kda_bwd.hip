@@ -170,6 +170,25 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         const int64_t rec = (rec0 + ci) * a.Hv + h;
         const int kb0 = 2 * wave;
 
+        // Global operands of the state-side products, issued before the
+        // prologue so that their latency hides behind it: this wave's
+        // chunk-start state frags, RF(U) and RF(dO) (zero past the end);
+        // S0 and dO stay in registers until the state update.
+        const int64_t tokc = tok0 + t0 + (kTail ? min(cl, nv - 1) : cl);  // RF row token
+        bf16x4 s0f[8][2], ru[8], rdo[8];
+        {
+            const bf16* dop = (const bf16*)b.d_o + tokc * a.Hv * D + h * D + 4 * gq;
+            const bf16* up = (const bf16*)a.rec_u + rec * REC_U + lane * 4;
+            const bf16* s0p = (const bf16*)a.rec_s0 + rec * REC_S0 + lane * 4;
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb) {
+                ru[vb] = *(const bf16x4*)(up + vb * 256);
+                rdo[vb] = *(const bf16x4*)(dop + 16 * vb);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) s0f[vb][j] = *(const bf16x4*)(s0p + ((kb0 + j) * 8 + vb) * 256);
+            }
+        }
+
         // ---- P1: norms, gate, beta (row-owner mapping); stage T, Akk, Aqk ----
         {
             float sq = 0.f, sk = 0.f;
@@ -258,19 +277,11 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         __syncthreads();
 
         // ---- M1 (per wave): state-side products with the incoming dS ----
-        // Streamed over pairs of value blocks so only one pair of S0, U and
-        // dO frags is live at a time.
         const bf16x4 ident = identity_frag(lane);
-        const int64_t tokc = tok0 + t0 + (kTail ? min(cl, nv - 1) : cl);  // RF row token
-        const bf16* dop = (const bf16*)b.d_o + tokc * a.Hv * D + h * D + 4 * gq;
-        const bf16* up = (const bf16*)a.rec_u + rec * REC_U + lane * 4;
-        const bf16* s0p = (const bf16*)a.rec_s0 + rec * REC_S0 + lane * 4;
-        // RF(dO)[vb]: lane (gq, c) holds dO[c][16vb + 4gq + i] (zero past the end)
-        auto load_rdo = [&](int vb) __attribute__((always_inline)) {
-            bf16x4 x = *(const bf16x4*)(dop + 16 * vb);
-            if (kTail && !valid_c) x = to_bf4(zero4());
-            return x;
-        };
+        if (kTail && !valid_c) {
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb) rdo[vb] = to_bf4(zero4());
+        }
         f32x4 dKtT[2] = {zero4(), zero4()};  // RF orientation: lane (gq, c) holds X[c][16kb + 4gq + i]
         f32x4 dQgT[2] = {zero4(), zero4()};
         f32x4 duOwn[2];
@@ -280,17 +291,14 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             float dgcacc[2] = {0.f, 0.f};
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                bf16x4 s0f[2][2], dsb[2][2], ru[2], rdo[2];
+                bf16x4 dsb[2][2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int vb = 2 * p + e;
-                    ru[e] = *(const bf16x4*)(up + vb * 256);
-                    rdo[e] = load_rdo(vb);
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        s0f[e][j] = *(const bf16x4*)(s0p + ((kb0 + j) * 8 + vb) * 256);
                         dsb[e][j] = to_bf4(dS[vb][j]);
-                        const f32x4 s0 = from_bf4(s0f[e][j]);
+                        const f32x4 s0 = from_bf4(s0f[vb][j]);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) dgcacc[j] += dS[vb][j][i] * s0[i];
                     }
@@ -309,10 +317,10 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 // dKt^T = dS^T U^T and dQg'^T = S0^T dO^T, contracting over v
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    dKtT[j] = mma32(cat8(dsb[0][j], dsb[1][j]), cat8(ru[0], ru[1]), dKtT[j]);
-                    dQgT[j] = mma32(cat8(s0f[0][j], s0f[1][j]), cat8(rdo[0], rdo[1]), dQgT[j]);
+                    dKtT[j] = mma32(cat8(dsb[0][j], dsb[1][j]), cat8(ru[2 * p], ru[2 * p + 1]), dKtT[j]);
+                    dQgT[j] = mma32(cat8(s0f[2 * p][j], s0f[2 * p + 1][j]), cat8(rdo[2 * p], rdo[2 * p + 1]), dQgT[j]);
                 }
-                daq = mma32(cat8(rdo[0], rdo[1]), cat8(ru[0], ru[1]), daq);
+                daq = mma32(cat8(rdo[2 * p], rdo[2 * p + 1]), cat8(ru[2 * p], ru[2 * p + 1]), daq);
             }
             // dgC from the state: sum over v of dS * S0, times exp(gC)
 #pragma unroll
@@ -335,6 +343,22 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         __syncthreads();
 
         // ---- R1 (per wave): finish dU for v-blocks 2w, 2w+1 ----
+        // V for this phase and raw q, k, g for the per-channel gradients
+        // (issued here, used after the dU reduction and two barriers later)
+        bf16x4 vv[2], qraw[2], kraw[2], graw[2];
+        {
+            const bf16* vp = (const bf16*)a.v + tokc * a.Hv * D + h * D + 32 * wave + 4 * gq;
+            vv[0] = *(const bf16x4*)vp;
+            vv[1] = *(const bf16x4*)(vp + 16);
+            const int64_t qo = tokc * a.Hqk * D + hq * D + 4 * gq;
+            const int64_t go = tokc * a.Hv * D + h * D + 4 * gq;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                qraw[j] = *(const bf16x4*)((const bf16*)a.q + qo + 16 * (kb0 + j));
+                kraw[j] = *(const bf16x4*)((const bf16*)a.k + qo + 16 * (kb0 + j));
+                graw[j] = *(const bf16x4*)((const bf16*)a.g + go + 16 * (kb0 + j));
+            }
+        }
         const f32x4 tB = ld4f(&sm.ta[0][cl][4 * gq]);  // frag(T): lane (gq, c) holds T[4gq+i][c]
         const bf16x4 tBb = to_bf4(tB);
         f32x4 dT;  // lane (gq, j) holds dT[4gq + i][j] (partial)
@@ -352,7 +376,11 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 f32x4 du = duOwn[jj];
 #pragma unroll
                 for (int s = 0; s < 3; ++s) du += sm.part[wave][s][jj][lane];
-                const bf16x4 cfdo = to_bf4(transpose_frag(load_rdo(vbo), ident));
+                bf16x4 rdv = rdo[0];  // RF(dO)[vbo], picked without dynamic indexing
+#pragma unroll
+                for (int v = 1; v < 8; ++v)
+                    if (v == vbo) rdv = rdo[v];
+                const bf16x4 cfdo = to_bf4(transpose_frag(rdv, ident));
                 du = mma16(cfdo, aqBb, du);  // + Aqk'^T dO
                 rfdu[jj] = to_bf4(du);
                 const bf16x4 cfdu = to_bf4(transpose_frag(rfdu[jj], ident));
@@ -361,13 +389,12 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 // dBv^T = dU^T T (RF orientation): lane (gq, c) holds (T^T dU)[c][16vbo + 4gq + i]
                 const f32x4 dbvT = mma16(cfdu, tBb, zero4());
                 const float bc = sm.beta[cl];
-                const bf16* vp = (const bf16*)a.v + tokc * a.Hv * D + h * D + 16 * vbo + 4 * gq;
-                const f32x4 vv = from_bf4(*(const bf16x4*)vp);
+                const f32x4 vvf = from_bf4(vv[jj]);
                 if (valid_c)
                     *(bf16x4*)((bf16*)b.dv + tokc * a.Hv * D + h * D + 16 * vbo + 4 * gq) = to_bf4(dbvT * bc);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dbv += dbvT[i] * vv[i];
-                bv[jj] = to_bf4(vv * bc);  // RF(beta V): lane (gq, j) holds beta_j V[j][..]
+                for (int i = 0; i < 4; ++i) dbv += dbvT[i] * vvf[i];
+                bv[jj] = to_bf4(vvf * bc);  // RF(beta V): lane (gq, j) holds beta_j V[j][..]
             }
             dbv = xor_sum_gq(dbv);
             if (gq == 0) sm.dbp[0][wave][cl] = dbv;
@@ -388,8 +415,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 f32x4 x = zero4();
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const bf16x8 s8 = cat8(*(const bf16x4*)(s0p + ((kb0 + j) * 8 + 2 * p) * 256),
-                                           *(const bf16x4*)(s0p + ((kb0 + j) * 8 + 2 * p + 1) * 256));
+                    const bf16x8 s8 = cat8(s0f[2 * p][j], s0f[2 * p + 1][j]);
                     x = mma32(s8, cat8(rfduA[2 * p], rfduA[2 * p + 1]), x);
                 }
                 dWb[j] = to_bf4(-x);  // RF(dW): lane (gq, c) holds dW[c][16kb + 4gq + i]
@@ -428,7 +454,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             for (int j = 0; j < 2; ++j) nw[j] = to_bf4(-wcf[j]);
 #pragma unroll
             for (int vb = 0; vb < 8; ++vb) {
-                const bf16x4 cfdo = to_bf4(transpose_frag(load_rdo(vb), ident));
+                const bf16x4 cfdo = to_bf4(transpose_frag(rdo[vb], ident));
                 const bf16x4 cfdu = ld4(&sm.cf_du[vb * FS], lane);
                 const bf16x8 a8 = cat8(cfdo, cfdu);
 #pragma unroll
@@ -489,9 +515,9 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int kbase = 16 * (kb0 + j) + 4 * gq;
-                const f32x4 qr = from_bf4(*(const bf16x4*)((const bf16*)a.q + qo + 16 * (kb0 + j)));
-                const f32x4 kr = from_bf4(*(const bf16x4*)((const bf16*)a.k + qo + 16 * (kb0 + j)));
-                const f32x4 gr = from_bf4(*(const bf16x4*)((const bf16*)a.g + go + 16 * (kb0 + j)));
+                const f32x4 qr = from_bf4(qraw[j]);
+                const f32x4 kr = from_bf4(kraw[j]);
+                const f32x4 gr = from_bf4(graw[j]);
                 const f32x4 gc = ld4f(&sm.lam[cl][kbase]);
                 const f32x4 gC = ld4f(&sm.gamc[kbase]);
                 const f32x4 dz4 = ld4f(&sm.dtz[kbase]);
