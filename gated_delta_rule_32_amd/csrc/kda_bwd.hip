@@ -113,7 +113,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     __shared__ BwdLds sm;
     const FwdArgs& a = b.f;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
 
     const int code = a.plan.task[blockIdx.x];
     const int n = code / a.Hv;
@@ -133,7 +133,12 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     // dS[16vb + 4gq + i][16kb + k]; starts at dfinal_state
     f32x4 dS[8][2];
     {
-        const int lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+        // addresses from an opaque copy of the thread id: the epilogue's
+        // dinitial_state stores use the same addresses, and the compiler
+        // would otherwise keep all 64 of them alive (spilled) through the loop
+        int tix = tid;
+        asm volatile("" : "+v"(tix));
+        const int lane = tix & 63, gq = lane >> 4, cl = lane & 15;
 #pragma unroll
         for (int vb = 0; vb < 8; ++vb)
 #pragma unroll
@@ -606,7 +611,9 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
 
     // dinitial_state, parameter partials
     {
-        const int lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+        int tix = tid;
+        asm volatile("" : "+v"(tix));
+        const int lane = tix & 63, gq = lane >> 4, cl = lane & 15;
 #pragma unroll
         for (int vb = 0; vb < 8; ++vb)
 #pragma unroll
