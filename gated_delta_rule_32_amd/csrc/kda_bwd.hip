@@ -180,6 +180,10 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         // chunk-start state frags, RF(U) and RF(dO) (zero past the end);
         // S0 and dO stay in registers until the state update.
         const int64_t tokc = tok0 + t0 + (kTail ? min(cl, nv - 1) : cl);  // RF row token
+        // the chunk's T^T, Akk^T, Aqk' record first (its LDS copy is made at
+        // the end of the prologue; loads complete in issue order)
+        float4 ta4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tix < REC_TA / 4) ta4 = ((const float4*)(a.rec_ta + rec * REC_TA))[tix];
         bf16x4 s0f[8][2], ru[8], rdo[8];
         {
             const bf16* dop = (const bf16*)b.d_o + tokc * a.Hv * D + h * D + 4 * gq;
@@ -220,8 +224,6 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 sm.rqn[r] = valid_r ? fast_rsqrt(sq + 1e-6f) : 0.f;
                 sm.rkn[r] = valid_r ? fast_rsqrt(sk + 1e-6f) : 0.f;
             }
-            if (tix < REC_TA / 4)
-                ((float4*)&sm.ta[0][0][0])[tix] = ((const float4*)(a.rec_ta + rec * REC_TA))[tix];
         }
         __syncthreads();
         // ---- P2: prefix sums over the chunk's tokens ----
@@ -277,6 +279,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             store_cf_pairs(sm.cf_kih, r, c8, kih4[0], kih4[1]);
             store_cf_pairs(sm.cf_kil, r, c8, kil4[0], kil4[1]);
         }
+        if (tix < REC_TA / 4) ((float4*)&sm.ta[0][0][0])[tix] = ta4;
         // the row inputs are dead: fetch the previous chunk's
         load_rows(cur, a, tok0 + max(t0 - CH + r, 0), hq, h, c8);
         __syncthreads();
