@@ -21,10 +21,10 @@
 // Work split.  One workgroup (4 waves) owns one (sequence, value head) task
 // for its whole length; wave w owns state columns v in [32w, 32w+32), held as
 // transposed 16x16 frags S^T[kb][vb] in FP32 registers.  The state path is
-// column-local, so no state crosses waves.  Three barriers per chunk: after
-// the gate (the prefix sums need every row), after the prefix sums, and after
-// the chunk's shared operands are in LDS; from there each wave works alone
-// (it redoes the small 16x16 algebra itself rather than wait for another).
+// column-local, so no state crosses waves.  Four barriers per chunk: after
+// the gate (the prefix sums need every row), after the prefix sums, after the
+// chunk's shared operands are in LDS, and after the chunk's 16x16 algebra
+// (Akk and the substitution on wave 0, Aqk on wave 1, shared through LDS).
 // Shared operands sit in LDS "frag slots" (64 lanes x 4 bf16, padded):
 //   RF(X)[kb]: lane (gq, c) holds X[c][16kb + 4gq + i]   (rows = tokens)
 //   CF(X)[kb]: lane (gq, k) holds X[4gq + i][16kb + k]   (tokens along i)
@@ -58,7 +58,7 @@ struct SolveScratch {        // used by wave 0 only: no barrier between its uses
 
 struct FwdLds {
     alignas(16) float lam[CH][D];   // log2-domain decays, then their in-chunk prefix sums
-    alignas(16) float gamc[D];      // exp(gC) per channel
+    alignas(16) float gamc[2][D];   // exp(gC) per channel, by chunk parity
     alignas(16) float dtz[D];       // dt_bias * exp(A_log) * log2(e)
     alignas(16) float beta[2][CH];  // double-buffered: a wave may start the next
                                     // chunk while another still solves with this one's
@@ -197,6 +197,77 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     }
     __syncthreads();
 
+    // ---- A: norms, gate and beta of chunk ci into LDS, 1/|q| and 1/|k| into
+    // registers; rows past the end of the sequence get zero operands and no
+    // decay.  Run for chunk ci+1 at the end of chunk ci's D1 phase (it
+    // touches nothing that phase reads), so its arithmetic overlaps the
+    // substitution and the MFMAs there; the D1 barrier publishes it.
+    auto phase_a = [&](const int ci, float& rq, float& rk) __attribute__((always_inline)) {
+        int tix = tid;
+        asm volatile("" : "+v"(tix));
+        const int r = tix >> 4;
+        const int c8 = (tix & 15) * 8;
+        // 1 for rows inside the sequence, else 0: multiplied in rather than
+        // selected, so that no branch splits the phase this runs inside
+        const float vm = r < L - ci * CH ? 1.0f : 0.0f;
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {  // BF16 pair dot products, FP32 sums
+            const bf16x2 q2 = {cur.q[i], cur.q[i + 1]}, k2 = {cur.k[i], cur.k[i + 1]};
+            sq = __builtin_amdgcn_fdot2_f32_bf16(q2, q2, sq, false);
+            sk = __builtin_amdgcn_fdot2_f32_bf16(k2, k2, sk, false);
+        }
+        sq = row16_sum(sq);
+        sk = row16_sum(sk);
+        // the output scale rides on the query norm: O = (s Qg) S0^T + (s Aqk) U
+        rq = (a.scale * vm) * fast_rsqrt(sq + 1e-6f);
+        rk = vm * fast_rsqrt(sk + 1e-6f);
+        float lv[8], dz[8];
+        *(float4*)&dz[0] = *(const float4*)&sm.dtz[c8];
+        *(float4*)&dz[4] = *(const float4*)&sm.dtz[c8 + 4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float e = __builtin_amdgcn_exp2f(-((float)cur.g[i] * zs + dz[i]));
+            lv[i] = ((-5.0f * LOG2E) * vm) * __builtin_amdgcn_rcpf(1.0f + e);
+        }
+        *(float4*)&sm.lam[r][c8] = make_float4(lv[0], lv[1], lv[2], lv[3]);
+        *(float4*)&sm.lam[r][c8 + 4] = make_float4(lv[4], lv[5], lv[6], lv[7]);
+        // the row's 16 lanes store the same value (no branch)
+        sm.beta[ci & 1][r] = vm * sigmoidf_((float)cur.b);
+    };
+    // ---- B: in-place prefix sums of chunk ci's decays over its tokens, and
+    // exp(gC).  Every wave takes 32 channels: lanes 0-31 sum rows 0-7, lanes
+    // 32-63 rows 8-15 and add the lower half's total, swapped across the
+    // wave's halves.  Run for chunk ci+1 inside chunk ci's last phase, after
+    // the barrier that publishes phase A. ----
+    auto phase_b = [&](const int ci) __attribute__((always_inline)) {
+        int tix = tid;
+        asm volatile("" : "+v"(tix));
+        const int lane = tix & 63;
+        const int ch = 32 * wave + (lane & 31);
+        const bool upper = lane >= 32;
+        const int r0 = upper ? 8 : 0;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = sm.lam[r0 + i][ch];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) x[i] += x[i - 1];
+        // upper lanes receive the lower half's total in [0], lower lanes the
+        // upper half's in [1]
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[7]), __float_as_uint(x[7]),
+                                                         false, false);
+        const float other = __uint_as_float(upper ? sw[0] : sw[1]);
+        const float off = upper ? other : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm.lam[r0 + i][ch] = x[i] + off;
+        // both halves hold the chunk total: the pair stores the same value
+        sm.gamc[ci & 1][ch] = __builtin_amdgcn_exp2f(x[7] + other);
+    };
+    float rq, rk;   // 1/sqrt(128)/|q| and 1/|k| of the chunk's row
+    phase_a(cb, rq, rk);
+    __syncthreads();
+    phase_b(cb);
+
     // One chunk; full chunks are compiled without the tail masks.
     auto chunk = [&](const int ci, auto tail_tag) __attribute__((always_inline)) {
         constexpr bool kTail = decltype(tail_tag)::value;
@@ -220,52 +291,14 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         set_prio_by_remaining(ce - ci, ce - cb);
         const int64_t rec = (rec0 + ci) * a.Hv + h;  // record index (rebuild only)
 
-        // ---- A: norms, gate, beta ----
-        float rq, rk;   // 1/sqrt(128)/|q| and 1/|k| (zero for rows past the end)
-        {
-            float sq = 0.f, sk = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float qv = (float)cur.q[i], kv = (float)cur.k[i];
-                sq += qv * qv;
-                sk += kv * kv;
-            }
-            sq = row16_sum(sq);
-            sk = row16_sum(sk);
-            // the output scale rides on the query norm: O = (s Qg) S0^T + (s Aqk) U
-            rq = valid ? a.scale * fast_rsqrt(sq + 1e-6f) : 0.f;
-            rk = valid ? fast_rsqrt(sk + 1e-6f) : 0.f;
-            float lv[8], dz[8];
-            *(float4*)&dz[0] = *(const float4*)&sm.dtz[c8];
-            *(float4*)&dz[4] = *(const float4*)&sm.dtz[c8 + 4];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float e = __builtin_amdgcn_exp2f(-((float)cur.g[i] * zs + dz[i]));
-                lv[i] = valid ? (-5.0f * LOG2E) * __builtin_amdgcn_rcpf(1.0f + e) : 0.f;
-            }
-            *(float4*)&sm.lam[r][c8] = make_float4(lv[0], lv[1], lv[2], lv[3]);
-            *(float4*)&sm.lam[r][c8 + 4] = make_float4(lv[4], lv[5], lv[6], lv[7]);
-            if ((tid & 15) == 0) sm.beta[ci & 1][r] = valid ? sigmoidf_((float)cur.b) : 0.f;
-        }
-        __syncthreads();
-        // ---- B: prefix sums over the chunk's tokens, per channel ----
-        if (tid < D) {
-            float acc = 0.f;
-#pragma unroll
-            for (int rr = 0; rr < CH; ++rr) {
-                acc += sm.lam[rr][tid];
-                sm.lam[rr][tid] = acc;
-            }
-            sm.gamc[tid] = __builtin_amdgcn_exp2f(acc);
-        }
-        __syncthreads();
+        __syncthreads();   // chunk ci's prefix sums, exp(gC) and beta are in LDS
         // ---- C: decay factors and the chunk's operands ----
         {
             float gc[8], gC[8];
             *(float4*)&gc[0] = *(const float4*)&sm.lam[r][c8];
             *(float4*)&gc[4] = *(const float4*)&sm.lam[r][c8 + 4];
-            *(float4*)&gC[0] = *(const float4*)&sm.gamc[c8];
-            *(float4*)&gC[4] = *(const float4*)&sm.gamc[c8 + 4];
+            *(float4*)&gC[0] = *(const float4*)&sm.gamc[ci & 1][c8];
+            *(float4*)&gC[4] = *(const float4*)&sm.gamc[ci & 1][c8 + 4];
             bf16x4 qg4[2], kg4[2], ki4[2], th4[2], tl4[2];
 #pragma unroll
             for (int s4 = 0; s4 < 2; ++s4) {
@@ -311,6 +344,43 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 
         // ---- D1: the chunk's 16x16 algebra once (wave 0: Akk and the
         // substitution; wave 1: Aqk), Y and O^T on every wave ----
+        // Y = Kg S0^T and O^T = S0 Qg^T (S0 converted once for both); every
+        // wave forms its own, waves 0 and 1 inside their branches so that
+        // these MFMAs fill the latency of the substitution
+        f32x4 Y[2] = {zero4(), zero4()};
+        f32x4 OT[2] = {zero4(), zero4()};
+        auto y_ot = [&]() __attribute__((always_inline)) {
+            bf16x8 sb[4][2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) {
+                    const bf16x4 s0 = to_bf4(S[2 * j][vb]);
+                    const bf16x4 s1 = to_bf4(S[2 * j + 1][vb]);
+                    sb[j][vb] = cat8(s0, s1);
+                    Y[vb] = mma32(kg8, sb[j][vb], Y[vb]);    // lane (gq, v) holds Y[4gq+i][v]
+                    if constexpr (kRebuild) {
+                        // chunk-start state record: frag (kb, vb) with lane (gq, k)
+                        // holding S0[16vb + 4gq + i][16kb + k]
+                        const bf16x4 ident = identity_frag(lane);
+                        const int vbg = 2 * wave + vb;
+                        bf16* dst = (bf16*)a.rec_s0 + rec * (D * D) + lane * 4;
+                        *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) = to_bf4(transpose_frag(s0, ident));
+                        *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) = to_bf4(transpose_frag(s1, ident));
+                    }
+                }
+            }
+            if constexpr (!kRebuild) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
+#pragma unroll
+                    for (int vb = 0; vb < 2; ++vb) OT[vb] = mma32(sb[j][vb], q8, OT[vb]);   // lane (gq, c): O[c][v=4gq+i]
+                }
+            }
+        };
+        float rq_next, rk_next;
         if (wave == 0) {
             SolveScratch& ws = sm.sv;
             f32x4 akk = zero4();
@@ -320,6 +390,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 const bf16x8 ki8 = cat8(ld4(&sm.rf_ki[(2 * j) * FS], lane), ld4(&sm.rf_ki[(2 * j + 1) * FS], lane));
                 akk = mma32(kg8, ki8, akk);     // lane (gq, c) holds Akk[4gq+i][c]
             }
+            y_ot();
             const float4 b4 = *(const float4*)&sm.beta[ci & 1][4 * gq];
             float4 col;  // column cl of N, rows 4gq..4gq+3
             col.x = (cl < 4 * gq + 0) ? b4.x * akk[0] : 0.f;
@@ -370,6 +441,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             split4(f32x4{t4.x, t4.y, t4.z, t4.w}, th4, tl4);
             *(bf16x4*)&sm.sh_tb[0][lane * 4] = th4;
             *(bf16x4*)&sm.sh_tb[1][lane * 4] = tl4;
+            phase_a(ci + 1, rq_next, rk_next);
         } else if (wave == 1) {
             // RF16(Aqk) = frag of Aqk^T = Ki Qg^T, causal part
             f32x4 aqkT = zero4();
@@ -379,6 +451,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 const bf16x8 qg8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
                 aqkT = mma32(ki8, qg8, aqkT);
             }
+            y_ot();
             f32x4 am;
 #pragma unroll
             for (int i = 0; i < 4; ++i) am[i] = (4 * gq + i <= cl) ? aqkT[i] : 0.f;
@@ -386,40 +459,10 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 *(float4*)(a.rec_ta + rec * 768 + 512 + cl * 16 + 4 * gq) = make_float4(am[0], am[1], am[2], am[3]);
             else
                 *(bf16x4*)&sm.sh_aq[lane * 4] = to_bf4(am);
-        }
-        // Y = Kg S0^T and O^T = S0 Qg^T (S0 converted once for both)
-        f32x4 Y[2] = {zero4(), zero4()};
-        f32x4 OT[2] = {zero4(), zero4()};
-        {
-            bf16x8 sb[4][2];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
-#pragma unroll
-                for (int vb = 0; vb < 2; ++vb) {
-                    const bf16x4 s0 = to_bf4(S[2 * j][vb]);
-                    const bf16x4 s1 = to_bf4(S[2 * j + 1][vb]);
-                    sb[j][vb] = cat8(s0, s1);
-                    Y[vb] = mma32(kg8, sb[j][vb], Y[vb]);    // lane (gq, v) holds Y[4gq+i][v]
-                    if constexpr (kRebuild) {
-                        // chunk-start state record: frag (kb, vb) with lane (gq, k)
-                        // holding S0[16vb + 4gq + i][16kb + k]
-                        const bf16x4 ident = identity_frag(lane);
-                        const int vbg = 2 * wave + vb;
-                        bf16* dst = (bf16*)a.rec_s0 + rec * (D * D) + lane * 4;
-                        *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) = to_bf4(transpose_frag(s0, ident));
-                        *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) = to_bf4(transpose_frag(s1, ident));
-                    }
-                }
-            }
-            if constexpr (!kRebuild) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bf16x8 q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
-#pragma unroll
-                    for (int vb = 0; vb < 2; ++vb) OT[vb] = mma32(sb[j][vb], q8, OT[vb]);   // lane (gq, c): O[c][v=4gq+i]
-                }
-            }
+            phase_a(ci + 1, rq_next, rk_next);
+        } else {
+            y_ot();
+            phase_a(ci + 1, rq_next, rk_next);
         }
         __syncthreads();
         // ---- D2 (per wave): U, output, state update ----
@@ -465,6 +508,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 *(bf16x4*)(sp.o + __umul24((unsigned)(t0 + cl), sp.sv) + 32 * wave + 16 * vb + 4 * gq) = ob;
             }
         }
+        phase_b(ci + 1);
         // (one accumulation chain keeps one MFMA shape: a 16x16x16 that reads
         // the accumulator of a 16x16x32 issued just before it has been seen
         // to miss that product)
@@ -472,7 +516,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         for (int kb = 0; kb < 8; ++kb) {
             const bf16x4 th = ld4(&sm.cf_kth[kb * FS], lane);
             const bf16x4 tl = ld4(&sm.cf_ktl[kb * FS], lane);
-            const float4 gd = *(const float4*)&sm.gamc[16 * kb + 4 * gq];
+            const float4 gd = *(const float4*)&sm.gamc[ci & 1][16 * kb + 4 * gq];
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb) {
                 f32x4 s = S[kb][vb];
@@ -488,6 +532,8 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             const int64_t jck = tend / a.ck_every;
             store_state(a.tape + ((tape_base + jck - 1) * a.Hv + h) * (int64_t)D * D, S, wave, gq, cl);
         }
+        rq = rq_next;
+        rk = rk_next;
     };
     const int cfull = min(ce, nfull);
     for (int ci = cb; ci < cfull; ++ci) chunk(ci, std::false_type{});
