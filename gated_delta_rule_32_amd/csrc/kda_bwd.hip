@@ -426,7 +426,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                     const bf16x8 s8 = cat8(s0f[2 * p][j], s0f[2 * p + 1][j]);
                     x = mma32(s8, cat8(rfduA[2 * p], rfduA[2 * p + 1]), x);
                 }
-                dWb[j] = to_bf4(-x);  // RF(dW): lane (gq, c) holds dW[c][16kb + 4gq + i]
+                dWb[j] = to_bf4_neg(x);  // RF(dW): lane (gq, c) holds dW[c][16kb + 4gq + i]
             }
             // dT += dW (beta Kg)^T over this wave's channels
             bf16x4 bk[2];
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             // dS <- dS exp(gC) + dO^T Qg' - dU^T W
             bf16x4 nw[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) nw[j] = to_bf4(-wcf[j]);
+            for (int j = 0; j < 2; ++j) nw[j] = to_bf4_neg(wcf[j]);
 #pragma unroll
             for (int vb = 0; vb < 8; ++vb) {
                 const bf16x4 cfdo = to_bf4(transpose_frag(rdo[vb], ident));

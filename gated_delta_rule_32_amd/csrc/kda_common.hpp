@@ -26,6 +26,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;          // head dimension (K = V = 128)
 constexpr int CH = 16;          // chunk length in tokens
@@ -57,8 +59,20 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// FP32 -> BF16, round to nearest even.  Converted pair by pair through a
+// 32-bit word: the compiler lowers a 4-wide vector truncation element by
+// element in some contexts (one conversion per element plus a repack),
+// while each pair here becomes one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ unsigned cvt_pk_bf16(float a, float b) {  // a in the low half
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
 __device__ __forceinline__ bf16x4 to_bf4(f32x4 x) {
-    return __builtin_convertvector(x, bf16x4);  // two v_cvt_pk_bf16_f32
+    return __builtin_bit_cast(bf16x4, u32x2{cvt_pk_bf16(x[0], x[1]), cvt_pk_bf16(x[2], x[3])});
+}
+// BF16 of -x: the sign flipped on the packed result (one integer op per pair).
+__device__ __forceinline__ bf16x4 to_bf4_neg(f32x4 x) {
+    return __builtin_bit_cast(bf16x4, u32x2{cvt_pk_bf16(x[0], x[1]) ^ 0x80008000u,
+                                            cvt_pk_bf16(x[2], x[3]) ^ 0x80008000u});
 }
 __device__ __forceinline__ f32x4 from_bf4(bf16x4 x) {
     return __builtin_convertvector(x, f32x4);
@@ -69,7 +83,6 @@ __device__ __forceinline__ f32x4 from_bf4(bf16x4 x) {
 // lo*hi' reproduces an FP32 product to ~2^-16 relative.
 __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
     const u32x4 u = __builtin_bit_cast(u32x4, x) & 0xffff0000u;
     const f32x4 h = __builtin_bit_cast(f32x4, u);
     // upper halves of (u0, u1) and (u2, u3) packed as bf16 pairs

@@ -482,10 +482,10 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             const bf16x4 cfv1 = to_bf4(mma16(vcur.v1, ident, zero4()));
             U[0] = mma16(tbh, cfv0, zero4());
             U[0] = mma16(tbl, cfv0, U[0]);
-            U[0] = mma16(tbh, to_bf4(-Y[0]), U[0]);
+            U[0] = mma16(tbh, to_bf4_neg(Y[0]), U[0]);
             U[1] = mma16(tbh, cfv1, zero4());
             U[1] = mma16(tbl, cfv1, U[1]);
-            U[1] = mma16(tbh, to_bf4(-Y[1]), U[1]);
+            U[1] = mma16(tbh, to_bf4_neg(Y[1]), U[1]);
         }
         load_cols_s(vcur, sp, min(t0 + CH + cl, L - 1), 32 * wave + 4 * gq);
         // O^T += U^T Aqk^T, store; then S update
