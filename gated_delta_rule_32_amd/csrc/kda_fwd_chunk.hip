@@ -51,9 +51,9 @@ namespace {
 constexpr int FC_THREADS = 256;
 constexpr int TBS = 20;  // row stride of the per-wave Tb scratch (16-byte rows)
 
-struct SolveScratch {        // used by wave 0 only: no barrier between its uses
-    alignas(16) float nT[CH][CH];   // nT[m][i] = beta_i Akk[i][m] for i > m, else 0
-    alignas(16) float tb[CH][TBS];  // Tb[i][j]
+struct SolveScratch {
+    alignas(16) float nT[CH][CH];   // nT[m][i] = beta_i Akk[i][m] for i > m, else 0 (wave 0 only)
+    alignas(16) float tb[CH][TBS];  // Tb[i][j], written by wave 0, read by all after a barrier
 };
 
 struct FwdLds {
@@ -63,7 +63,6 @@ struct FwdLds {
     alignas(16) float beta[2][CH];  // double-buffered: a wave may start the next
                                     // chunk while another still solves with this one's
     SolveScratch sv;
-    alignas(16) bf16 sh_tb[2][256]; // RF16(Tb) hi / lo frags, written by wave 0
     alignas(16) bf16 sh_aq[256];    // RF16(Aqk) frag, written by wave 1
     alignas(16) bf16 rf_qg[8 * FS];
     alignas(16) bf16 rf_kg[8 * FS];
@@ -418,15 +417,17 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             float y[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) y[j] = (4 * qd + j == colx) ? 1.0f : 0.0f;
+            // (step m changes only rows below m: the last step is empty, and
+            // element j, the rows 4q+j, is done once m reaches 12+j)
             float4 nxt = *(const float4*)&ws.nT[0][4 * qd];
 #pragma unroll
-            for (int m = 0; m < CH; ++m) {
+            for (int m = 0; m < CH - 1; ++m) {
                 const float4 nm = nxt;
-                if (m + 1 < CH) nxt = *(const float4*)&ws.nT[m + 1][4 * qd];
+                if (m + 1 < CH - 1) nxt = *(const float4*)&ws.nT[m + 1][4 * qd];
                 const float tm = quad_bcast(y[m & 3], m >> 2);
-                y[0] -= nm.x * tm;
-                y[1] -= nm.y * tm;
-                y[2] -= nm.z * tm;
+                if (m < 12) y[0] -= nm.x * tm;
+                if (m < 13) y[1] -= nm.y * tm;
+                if (m < 14) y[2] -= nm.z * tm;
                 y[3] -= nm.w * tm;
             }
             if (kRebuild)   // T^T[col][row]
@@ -435,12 +436,6 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             const float bc = sm.beta[ci & 1][colx];
 #pragma unroll
             for (int j = 0; j < 4; ++j) ws.tb[4 * qd + j][colx] = y[j] * bc;
-            // RF16(Tb) as a hi/lo pair: lane (gq, c) holds Tb[c][4gq+i]
-            const float4 t4 = *(const float4*)&ws.tb[cl][4 * gq];
-            bf16x4 th4, tl4;
-            split4(f32x4{t4.x, t4.y, t4.z, t4.w}, th4, tl4);
-            *(bf16x4*)&sm.sh_tb[0][lane * 4] = th4;
-            *(bf16x4*)&sm.sh_tb[1][lane * 4] = tl4;
             phase_a(ci + 1, rq_next, rk_next);
         } else if (wave == 1) {
             // RF16(Aqk) = frag of Aqk^T = Ki Qg^T, causal part
@@ -466,8 +461,13 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         }
         __syncthreads();
         // ---- D2 (per wave): U, output, state update ----
-        const bf16x4 tbh = ld4(&sm.sh_tb[0][0], lane);
-        const bf16x4 tbl = ld4(&sm.sh_tb[1][0], lane);
+        // RF16(Tb) as a hi/lo pair, split by every wave from wave 0's FP32 Tb
+        // (off the substitution's critical path): lane (gq, c) holds Tb[c][4gq+i]
+        bf16x4 tbh, tbl;
+        {
+            const float4 t4 = *(const float4*)&sm.sv.tb[cl][4 * gq];
+            split4(f32x4{t4.x, t4.y, t4.z, t4.w}, tbh, tbl);
+        }
         bf16x4 aq;
         if constexpr (!kRebuild) aq = ld4(&sm.sh_aq[0], lane);
         // CF(V) for the wave's columns (RF(V) times the identity, exact), then
