@@ -202,10 +202,10 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         {
             float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float qv = (float)cur.q[i], kv = (float)cur.k[i];
-                sq += qv * qv;
-                sk += kv * kv;
+            for (int i = 0; i < 8; i += 2) {  // BF16 pair dot products, FP32 sums
+                const bf16x2 q2 = {cur.q[i], cur.q[i + 1]}, k2 = {cur.k[i], cur.k[i + 1]};
+                sq = __builtin_amdgcn_fdot2_f32_bf16(q2, q2, sq, false);
+                sk = __builtin_amdgcn_fdot2_f32_bf16(k2, k2, sk, false);
             }
             sq = row16_sum(sq);
             sk = row16_sum(sk);
@@ -306,9 +306,14 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
                         dsb[e][j] = to_bf4(dS[vb][j]);
-                        const f32x4 s0 = from_bf4(s0f[vb][j]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) dgcacc[j] += dS[vb][j][i] * s0[i];
+                        // sum over v of dS * S0 as BF16 pair dot products
+                        const bf16x4 d = dsb[e][j], z = s0f[vb][j];
+                        dgcacc[j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(d, d, 0, 1),
+                                                                    __builtin_shufflevector(z, z, 0, 1),
+                                                                    dgcacc[j], false);
+                        dgcacc[j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(d, d, 2, 3),
+                                                                    __builtin_shufflevector(z, z, 2, 3),
+                                                                    dgcacc[j], false);
                     }
                     // dU over this wave's channels (RF orientation): A = dS with
                     // k along the rows (transposed frags), B = RF(Kt)
