@@ -273,11 +273,11 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 *(bf16x4*)&sm.rf_kt[orf + 64 * s] = kt4[s];
                 *(bf16x4*)&sm.rf_kg[orf + 64 * s] = kg4[s];
             }
-            store_cf_pairs(sm.cf_qh, r, c8, qh4[0], qh4[1]);
-            store_cf_pairs(sm.cf_ql, r, c8, ql4[0], ql4[1]);
-            store_cf_pairs(sm.cf_kg, r, c8, kg4[0], kg4[1]);
-            store_cf_pairs(sm.cf_kih, r, c8, kih4[0], kih4[1]);
-            store_cf_pairs(sm.cf_kil, r, c8, kil4[0], kil4[1]);
+            store_cf16(sm.cf_qh, r, c8, qh4[0], qh4[1]);
+            store_cf16(sm.cf_ql, r, c8, ql4[0], ql4[1]);
+            store_cf16(sm.cf_kg, r, c8, kg4[0], kg4[1]);
+            store_cf16(sm.cf_kih, r, c8, kih4[0], kih4[1]);
+            store_cf16(sm.cf_kil, r, c8, kil4[0], kil4[1]);
         }
         if (tix < REC_TA / 4) ((float4*)&sm.ta[0][0][0])[tix] = ta4;
         // the row inputs are dead: fetch the previous chunk's
@@ -537,20 +537,22 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 f32x4 dge, ktkt;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
+                    // with Kg = kn G, Ki = kn Gi, Kt = kn et and Qg' = scale qn G:
+                    //   dg_c = kn (dKg G - dKi Gi - dKt et) + qn dqn,  dqn = scale G dQg'
                     const float qn = qr[i] * rq, kn = kr[i] * rk;
                     const float G = __builtin_amdgcn_exp2f(gc[i]);
                     const float Gi = __builtin_amdgcn_exp2f(-gc[i]);
                     const float et = gC[i] * Gi;
-                    const float Qg = scale * qn * G, Kg = kn * G, Ki = kn * Gi, Kt = kn * et;
-                    const float dKt = dKtT[j][i], dKg = dKgT[j][i], dKi = dKiT[j][i], dQg = dQgT[j][i];
-                    dkn4[j][i] = dKt * et + dKg * G + dKi * Gi;
-                    dqn4[j][i] = scale * G * dQg;
-                    dge[i] = -dKt * Kt + dKg * Kg - dKi * Ki + dQg * Qg;
-                    ktkt[i] = dKt * Kt;
+                    const float ta = dKtT[j][i] * et, tb = dKgT[j][i] * G, tc = dKiT[j][i] * Gi;
+                    dkn4[j][i] = ta + tb + tc;
+                    dqn4[j][i] = (scale * dQgT[j][i]) * G;
+                    const float pq = qn * dqn4[j][i];
+                    dge[i] = kn * (tb - ta - tc) + pq;
+                    ktkt[i] = kn * ta;
                     qn4[j][i] = qn;
                     kn4[j][i] = kn;
                     zl4[j][i] = gr[i] * zs + dz4[i];
-                    dotq += qn * dqn4[j][i];
+                    dotq += pq;
                     dotk += kn * dkn4[j][i];
                 }
 #pragma unroll

@@ -37,32 +37,15 @@ __device__ __forceinline__ void load_rows(RowIn& x, const FwdArgs& a, int64_t to
     x.g = *(const bf16x8*)((const bf16*)a.g + tok * a.Hv * D + h * D + c8);
     x.b = ((const bf16*)a.beta)[tok * a.Hv + h];
 }
-// Column-layout stores of one 4-channel group for a pair of token rows.
-// Rows c (even) and c+1 sit in lane rows 2p and 2p+1 of the wave; after one
-// lane-row swap the even row's lanes hold both rows' values for channels
-// c8+4..c8+7 and the odd row's lanes for c8..c8+3, so each lane writes four
-// (row c, row c+1) pairs as 32-bit words (the two rows are adjacent in CF).
-__device__ __forceinline__ void store_cf_pairs(bf16* slots, int r, int c8, bf16x4 lo, bf16x4 hi) {
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 ulo = __builtin_bit_cast(u32x2, lo);
-    const u32x2 uhi = __builtin_bit_cast(u32x2, hi);
-    // swap(a = hi, b = lo): lane row 2p receives row 2p+1's `hi` in the second
-    // result, lane row 2p+1 receives row 2p's `lo` in the first.
-    const auto s0 = __builtin_amdgcn_permlane16_swap(uhi[0], ulo[0], false, false);
-    const auto s1 = __builtin_amdgcn_permlane16_swap(uhi[1], ulo[1], false, false);
-    const bool even = (r & 1) == 0;
-    const u32x2 p = even ? u32x2{s0[1], s1[1]} : u32x2{s0[0], s1[0]};
-    const u32x2 m = even ? uhi : ulo;
-    // (even-row value, odd-row value) pairs: the even row's bf16 goes to the
-    // low half; byte selectors for the low / high bf16 of each source word
-    const unsigned sel_lo = even ? 0x05040100u : 0x01000504u;
-    const unsigned sel_hi = even ? 0x07060302u : 0x03020706u;
-    const int kbase = c8 + (even ? 4 : 0);
-    unsigned* dst = (unsigned*)&slots[cf_off(r & ~1, kbase)];  // channel kbase+j at +2j words
-    dst[0] = __builtin_amdgcn_perm(p[0], m[0], sel_lo);
-    dst[2] = __builtin_amdgcn_perm(p[0], m[0], sel_hi);
-    dst[4] = __builtin_amdgcn_perm(p[1], m[1], sel_lo);
-    dst[6] = __builtin_amdgcn_perm(p[1], m[1], sel_hi);
+// Column-layout stores of one token row's 8 channels (c8..c8+7, one 16-channel
+// block) as single BF16 values: channel c8 + j sits 4j elements after c8.
+__device__ __forceinline__ void store_cf16(bf16* slots, int r, int c8, bf16x4 lo, bf16x4 hi) {
+    bf16* dst = &slots[cf_off(r, c8)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        dst[4 * j] = lo[j];
+        dst[4 * (j + 4)] = hi[j];
+    }
 }
 
 // Broadcast lane q of every quad to the whole quad (DPP quad_perm [q,q,q,q]);
