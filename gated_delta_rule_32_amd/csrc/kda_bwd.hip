@@ -128,6 +128,31 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     const float eA = __expf(a.A_log[h]);
     const float zs = eA * LOG2E;
     const float scale = a.scale;
+    // Per-task base pointers (uniform, so they live in scalar registers) and
+    // per-token element strides: a token inside the sequence is then a 32-bit
+    // row offset (the host rejects sequences spanning 2^31 elements or more).
+    const unsigned sq = (unsigned)(a.Hqk * D), sv = (unsigned)(a.Hv * D), sb = (unsigned)a.Hv;
+    const int64_t qk0 = (tok0 * a.Hqk + hq) * D, vh0 = (tok0 * a.Hv + h) * D, bh0 = tok0 * a.Hv + h;
+    const bf16* const qp = (const bf16*)a.q + qk0;
+    const bf16* const kp = (const bf16*)a.k + qk0;
+    const bf16* const gp = (const bf16*)a.g + vh0;
+    const bf16* const vp0 = (const bf16*)a.v + vh0;
+    const bf16* const dop0 = (const bf16*)b.d_o + vh0;
+    const bf16* const betap = (const bf16*)a.beta + bh0;
+    bf16* const dvp = (bf16*)b.dv + vh0;
+    bf16* const dgp = (bf16*)b.dg + vh0;
+    bf16* const dqp = (bf16*)b.dq + qk0;
+    bf16* const dkp = (bf16*)b.dk + qk0;
+    bf16* const dbetap = (bf16*)b.dbeta + bh0;
+    float* const dqkp = b.dqk_part != nullptr ? b.dqk_part + vh0 * 2 : nullptr;
+    // one token row (8 channels at c8) of q, k, g and its beta logit
+    auto load_row = [&](RowIn& x, int t, int c8) __attribute__((always_inline)) {
+        const unsigned oq = __umul24((unsigned)t, sq) + c8;
+        x.q = *(const bf16x8*)(qp + oq);
+        x.k = *(const bf16x8*)(kp + oq);
+        x.g = *(const bf16x8*)(gp + __umul24((unsigned)t, sv) + c8);
+        x.b = betap[__umul24((unsigned)t, sb)];
+    };
 
     // dS frags: dS[vb][j] for kb = 2*wave + j, lane (gq, k) holds
     // dS[16vb + 4gq + i][16kb + k]; starts at dfinal_state
@@ -156,7 +181,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     float dA_acc = 0.f;
 
     RowIn cur;
-    load_rows(cur, a, tok0 + min((nchunks - 1) * CH + (tid >> 4), L - 1), hq, h, (tid & 15) * 8);
+    load_row(cur, min((nchunks - 1) * CH + (tid >> 4), L - 1), (tid & 15) * 8);
     __syncthreads();
 
     auto chunk = [&](const int ci, auto tail_tag) __attribute__((always_inline)) {
@@ -179,14 +204,15 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         // prologue so that their latency hides behind it: this wave's
         // chunk-start state frags, RF(U) and RF(dO) (zero past the end);
         // S0 and dO stay in registers until the state update.
-        const int64_t tokc = tok0 + t0 + (kTail ? min(cl, nv - 1) : cl);  // RF row token
+        const unsigned tc = (unsigned)(t0 + (kTail ? min(cl, nv - 1) : cl));  // RF row token
+        const unsigned ov = __umul24(tc, sv), oq = __umul24(tc, sq);          // its row offsets
         // the chunk's T^T, Akk^T, Aqk' record first (its LDS copy is made at
         // the end of the prologue; loads complete in issue order)
         float4 ta4 = make_float4(0.f, 0.f, 0.f, 0.f);
         if (tix < REC_TA / 4) ta4 = ((const float4*)(a.rec_ta + rec * REC_TA))[tix];
         bf16x4 s0f[8][2], ru[8], rdo[8];
         {
-            const bf16* dop = (const bf16*)b.d_o + tokc * a.Hv * D + h * D + 4 * gq;
+            const bf16* dop = dop0 + ov + 4 * gq;
             const bf16* up = (const bf16*)a.rec_u + rec * REC_U + lane * 4;
             const bf16* s0p = (const bf16*)a.rec_s0 + rec * REC_S0 + lane * 4;
 #pragma unroll
@@ -281,7 +307,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         }
         if (tix < REC_TA / 4) ((float4*)&sm.ta[0][0][0])[tix] = ta4;
         // the row inputs are dead: fetch the previous chunk's
-        load_rows(cur, a, tok0 + max(t0 - CH + r, 0), hq, h, c8);
+        load_row(cur, max(t0 - CH + r, 0), c8);
         __syncthreads();
 
         // ---- M1 (per wave): state-side products with the incoming dS ----
@@ -360,16 +386,14 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         // (issued here, used after the dU reduction and two barriers later)
         bf16x4 vv[2], qraw[2], kraw[2], graw[2];
         {
-            const bf16* vp = (const bf16*)a.v + tokc * a.Hv * D + h * D + 32 * wave + 4 * gq;
+            const bf16* vp = vp0 + ov + 32 * wave + 4 * gq;
             vv[0] = *(const bf16x4*)vp;
             vv[1] = *(const bf16x4*)(vp + 16);
-            const int64_t qo = tokc * a.Hqk * D + hq * D + 4 * gq;
-            const int64_t go = tokc * a.Hv * D + h * D + 4 * gq;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                qraw[j] = *(const bf16x4*)((const bf16*)a.q + qo + 16 * (kb0 + j));
-                kraw[j] = *(const bf16x4*)((const bf16*)a.k + qo + 16 * (kb0 + j));
-                graw[j] = *(const bf16x4*)((const bf16*)a.g + go + 16 * (kb0 + j));
+                qraw[j] = *(const bf16x4*)(qp + oq + 16 * (kb0 + j) + 4 * gq);
+                kraw[j] = *(const bf16x4*)(kp + oq + 16 * (kb0 + j) + 4 * gq);
+                graw[j] = *(const bf16x4*)(gp + ov + 16 * (kb0 + j) + 4 * gq);
             }
         }
         const f32x4 tB = ld4f(&sm.ta[0][cl][4 * gq]);  // frag(T): lane (gq, c) holds T[4gq+i][c]
@@ -404,7 +428,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 const float bc = sm.beta[cl];
                 const f32x4 vvf = from_bf4(vv[jj]);
                 if (valid_c)
-                    *(bf16x4*)((bf16*)b.dv + tokc * a.Hv * D + h * D + 16 * vbo + 4 * gq) = to_bf4(dbvT * bc);
+                    *(bf16x4*)(dvp + ov + 16 * vbo + 4 * gq) = to_bf4(dbvT * bc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dbv += dbvT[i] * vvf[i];
                 bv[jj] = to_bf4(vvf * bc);  // RF(beta V): lane (gq, j) holds beta_j V[j][..]
@@ -522,8 +546,6 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         f32x4 qn4[2], kn4[2], dqn4[2], dkn4[2], dlam4[2], zl4[2];
         {
             const float rq = sm.rqn[cl], rk = sm.rkn[cl];
-            const int64_t qo = tokc * a.Hqk * D + hq * D + 4 * gq;
-            const int64_t go = tokc * a.Hv * D + h * D + 4 * gq;
             float dotq = 0.f, dotk = 0.f;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -575,10 +597,9 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             const float rq = sm.rqn[cl], rk = sm.rkn[cl];
             const float dotq = sm.dots[0][0][cl] + sm.dots[1][0][cl] + sm.dots[2][0][cl] + sm.dots[3][0][cl];
             const float dotk = sm.dots[0][1][cl] + sm.dots[1][1][cl] + sm.dots[2][1][cl] + sm.dots[3][1][cl];
-            const int64_t go = tokc * a.Hv * D + h * D + 4 * gq;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int koff = 16 * (kb0 + j);
+                const int koff = 16 * (kb0 + j) + 4 * gq;
                 f32x4 dgo, dq, dk;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -593,13 +614,12 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                     }
                 }
                 if (valid_c) {
-                    *(bf16x4*)((bf16*)b.dg + go + koff) = to_bf4(dgo);
-                    if (b.dqk_part == nullptr) {
-                        const int64_t qo = tokc * a.Hqk * D + hq * D + 4 * gq + koff;
-                        *(bf16x4*)((bf16*)b.dq + qo) = to_bf4(dq);
-                        *(bf16x4*)((bf16*)b.dk + qo) = to_bf4(dk);
+                    *(bf16x4*)(dgp + ov + koff) = to_bf4(dgo);
+                    if (dqkp == nullptr) {
+                        *(bf16x4*)(dqp + oq + koff) = to_bf4(dq);
+                        *(bf16x4*)(dkp + oq + koff) = to_bf4(dk);
                     } else {
-                        float* pp = b.dqk_part + (tokc * a.Hv + h) * (2 * D) + 4 * gq + koff;
+                        float* pp = dqkp + 2 * ov + koff;
                         *(float4*)pp = make_float4(dq[0], dq[1], dq[2], dq[3]);
                         *(float4*)(pp + D) = make_float4(dk[0], dk[1], dk[2], dk[3]);
                     }
@@ -611,7 +631,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                                  sm.dba[cl];
                 const float bt = sm.beta[cl];
                 // dbeta on the logit: db * sigma'(x) = db * beta (1 - beta)
-                ((bf16*)b.dbeta)[tokc * a.Hv + h] = (bf16)(db * bt * (1.0f - bt));
+                dbetap[__umul24(tc, sb)] = (bf16)(db * bt * (1.0f - bt));
             }
         }
         __syncthreads();
