@@ -148,10 +148,10 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     // one token row (8 channels at c8) of q, k, g and its beta logit
     auto load_row = [&](RowIn& x, int t, int c8) __attribute__((always_inline)) {
         const unsigned oq = __umul24((unsigned)t, sq) + c8;
-        x.q = *(const bf16x8*)(qp + oq);
-        x.k = *(const bf16x8*)(kp + oq);
-        x.g = *(const bf16x8*)(gp + __umul24((unsigned)t, sv) + c8);
-        x.b = betap[__umul24((unsigned)t, sb)];
+        x.q = *(const bf16x8*)at(qp, oq);
+        x.k = *(const bf16x8*)at(kp, oq);
+        x.g = *(const bf16x8*)at(gp, __umul24((unsigned)t, sv) + c8);
+        x.b = *at(betap, __umul24((unsigned)t, sb));
     };
 
     // dS frags: dS[vb][j] for kb = 2*wave + j, lane (gq, k) holds
@@ -209,18 +209,18 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         // the chunk's T^T, Akk^T, Aqk' record first (its LDS copy is made at
         // the end of the prologue; loads complete in issue order)
         float4 ta4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tix < REC_TA / 4) ta4 = ((const float4*)(a.rec_ta + rec * REC_TA))[tix];
+        if (tix < REC_TA / 4) ta4 = *(const float4*)at(a.rec_ta + rec * REC_TA, 4 * tix);
         bf16x4 s0f[8][2], ru[8], rdo[8];
         {
-            const bf16* dop = dop0 + ov + 4 * gq;
-            const bf16* up = (const bf16*)a.rec_u + rec * REC_U + lane * 4;
-            const bf16* s0p = (const bf16*)a.rec_s0 + rec * REC_S0 + lane * 4;
+            const bf16* up = (const bf16*)a.rec_u + rec * REC_U;      // uniform record bases
+            const bf16* s0p = (const bf16*)a.rec_s0 + rec * REC_S0;
 #pragma unroll
             for (int vb = 0; vb < 8; ++vb) {
-                ru[vb] = *(const bf16x4*)(up + vb * 256);
-                rdo[vb] = *(const bf16x4*)(dop + 16 * vb);
+                ru[vb] = *(const bf16x4*)at(up, vb * 256 + lane * 4);
+                rdo[vb] = *(const bf16x4*)at(dop0, ov + 16 * vb + 4 * gq);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) s0f[vb][j] = *(const bf16x4*)(s0p + ((kb0 + j) * 8 + vb) * 256);
+                for (int j = 0; j < 2; ++j)
+                    s0f[vb][j] = *(const bf16x4*)at(s0p, ((kb0 + j) * 8 + vb) * 256 + lane * 4);
             }
         }
 
@@ -386,14 +386,13 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         // (issued here, used after the dU reduction and two barriers later)
         bf16x4 vv[2], qraw[2], kraw[2], graw[2];
         {
-            const bf16* vp = vp0 + ov + 32 * wave + 4 * gq;
-            vv[0] = *(const bf16x4*)vp;
-            vv[1] = *(const bf16x4*)(vp + 16);
+            vv[0] = *(const bf16x4*)at(vp0, ov + 32 * wave + 4 * gq);
+            vv[1] = *(const bf16x4*)at(vp0, ov + 32 * wave + 16 + 4 * gq);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                qraw[j] = *(const bf16x4*)(qp + oq + 16 * (kb0 + j) + 4 * gq);
-                kraw[j] = *(const bf16x4*)(kp + oq + 16 * (kb0 + j) + 4 * gq);
-                graw[j] = *(const bf16x4*)(gp + ov + 16 * (kb0 + j) + 4 * gq);
+                qraw[j] = *(const bf16x4*)at(qp, oq + 16 * (kb0 + j) + 4 * gq);
+                kraw[j] = *(const bf16x4*)at(kp, oq + 16 * (kb0 + j) + 4 * gq);
+                graw[j] = *(const bf16x4*)at(gp, ov + 16 * (kb0 + j) + 4 * gq);
             }
         }
         const f32x4 tB = ld4f(&sm.ta[0][cl][4 * gq]);  // frag(T): lane (gq, c) holds T[4gq+i][c]
@@ -428,7 +427,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 const float bc = sm.beta[cl];
                 const f32x4 vvf = from_bf4(vv[jj]);
                 if (valid_c)
-                    *(bf16x4*)(dvp + ov + 16 * vbo + 4 * gq) = to_bf4(dbvT * bc);
+                    *(bf16x4*)at(dvp, ov + 16 * vbo + 4 * gq) = to_bf4(dbvT * bc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dbv += dbvT[i] * vvf[i];
                 bv[jj] = to_bf4(vvf * bc);  // RF(beta V): lane (gq, j) holds beta_j V[j][..]
@@ -614,10 +613,10 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                     }
                 }
                 if (valid_c) {
-                    *(bf16x4*)(dgp + ov + koff) = to_bf4(dgo);
+                    *(bf16x4*)at(dgp, ov + koff) = to_bf4(dgo);
                     if (dqkp == nullptr) {
-                        *(bf16x4*)(dqp + oq + koff) = to_bf4(dq);
-                        *(bf16x4*)(dkp + oq + koff) = to_bf4(dk);
+                        *(bf16x4*)at(dqp, oq + koff) = to_bf4(dq);
+                        *(bf16x4*)at(dkp, oq + koff) = to_bf4(dk);
                     } else {
                         float* pp = dqkp + 2 * ov + koff;
                         *(float4*)pp = make_float4(dq[0], dq[1], dq[2], dq[3]);
@@ -631,7 +630,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                                  sm.dba[cl];
                 const float bt = sm.beta[cl];
                 // dbeta on the logit: db * sigma'(x) = db * beta (1 - beta)
-                dbetap[__umul24(tc, sb)] = (bf16)(db * bt * (1.0f - bt));
+                *at(dbetap, __umul24(tc, sb)) = (bf16)(db * bt * (1.0f - bt));
             }
         }
         __syncthreads();

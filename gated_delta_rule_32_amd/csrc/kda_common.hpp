@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
 
 typedef __bf16 bf16;
@@ -90,6 +92,15 @@ __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
                       __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
     hi = __builtin_bit_cast(bf16x4, hp);
     lo = to_bf4(x - h);
+}
+
+// base + off elements with the byte offset formed in 32 bits, so that the
+// access can use a scalar base and a 32-bit vector offset instead of 64-bit
+// per-lane address arithmetic (off * sizeof(T) must stay below 2^32).
+template <class T>
+__device__ __forceinline__ T* at(T* base, unsigned off) {
+    typedef typename std::conditional<std::is_const<T>::value, const char, char>::type C;
+    return reinterpret_cast<T*>(reinterpret_cast<C*>(base) + off * (unsigned)sizeof(T));
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }

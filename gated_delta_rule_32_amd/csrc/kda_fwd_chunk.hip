@@ -90,15 +90,15 @@ struct SeqPtrs {
 
 __device__ __forceinline__ void load_rows_s(RowIn& x, const SeqPtrs& p, unsigned t, unsigned c8) {
     const unsigned oq = __umul24(t, p.sq) + c8;
-    x.q = *(const bf16x8*)(p.q + oq);
-    x.k = *(const bf16x8*)(p.k + oq);
-    x.g = *(const bf16x8*)(p.g + __umul24(t, p.sv) + c8);
-    x.b = p.beta[__umul24(t, p.sb)];
+    x.q = *(const bf16x8*)at(p.q, oq);
+    x.k = *(const bf16x8*)at(p.k, oq);
+    x.g = *(const bf16x8*)at(p.g, __umul24(t, p.sv) + c8);
+    x.b = *at(p.beta, __umul24(t, p.sb));
 }
 __device__ __forceinline__ void load_cols_s(ColIn& x, const SeqPtrs& p, unsigned t, unsigned ch0) {
-    const bf16* q = p.v + __umul24(t, p.sv) + ch0;
-    x.v0 = *(const bf16x4*)q;
-    x.v1 = *(const bf16x4*)(q + 16);
+    const unsigned o = __umul24(t, p.sv) + ch0;
+    x.v0 = *(const bf16x4*)at(p.v, o);
+    x.v1 = *(const bf16x4*)at(p.v, o + 16);
 }
 
 __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], int wave, int gq,
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 m.y = (cl < 4 * gq + 1) ? akk[1] : 0.f;
                 m.z = (cl < 4 * gq + 2) ? akk[2] : 0.f;
                 m.w = (cl < 4 * gq + 3) ? akk[3] : 0.f;
-                *(float4*)(a.rec_ta + rec * 768 + 256 + cl * 16 + 4 * gq) = m;
+                *(float4*)at(a.rec_ta + rec * 768, 256 + cl * 16 + 4 * gq) = m;
             }
             // T = (I + N)^-1 by right-looking substitution on all 64 lanes:
             // lane (col = lane/4, q = lane%4) keeps rows 4q..4q+3 of column
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 y[3] -= nm.w * tm;
             }
             if (kRebuild)   // T^T[col][row]
-                *(float4*)(a.rec_ta + rec * 768 + colx * 16 + 4 * qd) = make_float4(y[0], y[1], y[2], y[3]);
+                *(float4*)at(a.rec_ta + rec * 768, colx * 16 + 4 * qd) = make_float4(y[0], y[1], y[2], y[3]);
             // Tb[i][col] = T[i][col] beta_col
             const float bc = sm.beta[ci & 1][colx];
 #pragma unroll
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) am[i] = (4 * gq + i <= cl) ? aqkT[i] : 0.f;
             if constexpr (kRebuild)   // Aqk[row = cl][col = 4gq + i], scale included
-                *(float4*)(a.rec_ta + rec * 768 + 512 + cl * 16 + 4 * gq) = make_float4(am[0], am[1], am[2], am[3]);
+                *(float4*)at(a.rec_ta + rec * 768, 512 + cl * 16 + 4 * gq) = make_float4(am[0], am[1], am[2], am[3]);
             else
                 *(bf16x4*)&sm.sh_aq[lane * 4] = to_bf4(am);
             phase_a(ci + 1, rq_next, rk_next);
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             if constexpr (kRebuild) {
                 // U record, RF layout: lane (gq, c) holds U[c][16vb + 4gq + i]
                 const bf16x4 ut = to_bf4(transpose_frag(to_bf4(U[vb]), identity_frag(lane)));
-                *(bf16x4*)((bf16*)a.rec_u + rec * (CH * D) + ((2 * wave + vb) * 64 + lane) * 4) = ut;
+                *(bf16x4*)at((bf16*)a.rec_u + rec * (CH * D), ((2 * wave + vb) * 64 + lane) * 4) = ut;
                 continue;
             }
             // the chain's last step is a 16x16x32 as well (upper half zero)
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             // lane (gq, c) holds O[c][32w + 16vb + 4gq + i]
             if (cl < nv) {
                 const bf16x4 ob = to_bf4(OT[vb]);
-                *(bf16x4*)(sp.o + __umul24((unsigned)(t0 + cl), sp.sv) + 32 * wave + 16 * vb + 4 * gq) = ob;
+                *(bf16x4*)at(sp.o, __umul24((unsigned)(t0 + cl), sp.sv) + 32 * wave + 16 * vb + 4 * gq) = ob;
             }
         }
         phase_b(ci + 1);
