@@ -3,9 +3,11 @@ and compare with the FP64 oracle at the tolerances the method fixes.
 
 Tolerances: o and every gradient elementwise |x - ref| <= 1e-2 + 1e-2 |ref|
 (page "flashinfer.kda_training", paragraph 6: validation bar), and, because
-that bar is loose against these magnitudes, relative Frobenius error
-||x - ref|| / ||ref|| <= 1e-2 as well; the FP32 final state within max-abs
-1e-3.
+that bar is loose against these magnitudes, a Frobenius bar as well:
+||x - ref|| <= 1e-2 ||ref|| + 1e-6 sqrt(n) (relative, with an absolute floor
+of 1e-6 RMS so that a reference that is zero to within underflow, such as a
+gate gradient through a saturated sigmoid, does not demand exact zeros); the
+FP32 final state within max-abs 1e-3.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ import workloads
 
 ATOL = RTOL = 1e-2
 FROB = 1e-2
+FROB_ABS = 1e-6   # RMS floor of the Frobenius bar
 STATE_ATOL = 1e-3
 
 
@@ -46,7 +49,8 @@ def oracle_backward(inp: workloads.Inputs, tasks=None, workers=None):
 
 
 def errors(x, ref):
-    """(max elementwise violation ratio, relative Frobenius error, max abs error)."""
+    """(max elementwise violation ratio, relative Frobenius error, max abs
+    error, Frobenius violation ratio: error over the Frobenius bar)."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     m = ~np.isnan(ref)
@@ -54,14 +58,16 @@ def errors(x, ref):
     diff = np.abs(x - ref)
     viol = float(np.max(diff / (ATOL + RTOL * np.abs(ref)))) if diff.size else 0.0
     nrm = float(np.linalg.norm(ref))
-    frob = float(np.linalg.norm(x - ref) / nrm) if nrm > 0 else float(np.linalg.norm(x - ref))
-    return viol, frob, float(diff.max()) if diff.size else 0.0
+    err = float(np.linalg.norm(x - ref))
+    frob = err / nrm if nrm > 0 else err
+    fviol = err / (FROB * nrm + FROB_ABS * np.sqrt(max(diff.size, 1)))
+    return viol, frob, float(diff.max()) if diff.size else 0.0, fviol
 
 
-def assert_close(name, x, ref, frob=FROB):
-    viol, fr, mx = errors(x, ref)
+def assert_close(name, x, ref):
+    viol, fr, mx, fviol = errors(x, ref)
     assert viol <= 1.0, f"{name}: elementwise bar exceeded (worst ratio {viol:.3g}, max abs {mx:.3g})"
-    assert fr <= frob, f"{name}: relative Frobenius error {fr:.3g} > {frob}"
+    assert fviol <= 1.0, f"{name}: Frobenius bar exceeded (relative error {fr:.3g})"
     return viol, fr, mx
 
 
@@ -72,6 +78,32 @@ def assert_state_close(name, x, ref, atol=STATE_ATOL):
     mx = float(np.abs(x[m] - ref[m]).max())
     assert mx <= atol, f"{name}: max-abs error {mx:.3g} > {atol}"
     return mx
+
+
+GRAD_NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dA_log", "ddt_bias", "dinitial_state")
+
+
+def run_backward(inp: workloads.Inputs, route: int = 0, ckpt: int = 0):
+    """Forward with context, then the paired backward; the eight gradients as
+    NumPy FP32 arrays."""
+    import gated_delta_rule_32_amd as kda
+    o, fs, ctx, d = run_forward(inp, route=route, ckpt=ckpt, save_context=True)
+    grads = kda.recurrent_kda_training_backward(ctx, d.do, d.dfinal_state)
+    torch.cuda.synchronize()
+    return [g.float().cpu().numpy() for g in grads]
+
+
+def report_and_check(pairs):
+    """pairs: (name, got, ref) triples.  Prints every error, then asserts the
+    elementwise and Frobenius bars."""
+    rows = []
+    for name, x, r in pairs:
+        viol, fr, mx, fviol = errors(x, r)
+        rows.append((name, viol, fr, mx, fviol))
+        print(f"  {name:16s} worst ratio {viol:.3g}  rel-frob {fr:.3g}  max-abs {mx:.3g}", flush=True)
+    for name, viol, fr, mx, fviol in rows:
+        assert viol <= 1.0, f"{name}: elementwise bar exceeded (worst ratio {viol:.3g}, max abs {mx:.3g})"
+        assert fviol <= 1.0, f"{name}: Frobenius bar exceeded (relative error {fr:.3g})"
 
 
 def task_mask_tokens(problem, tasks):

@@ -151,3 +151,14 @@ def test_backward_rejects_unknown_context():
     # no forward recorded this context: rejected (after no device work besides
     # querying the current device, which may itself fail on a GPU-less host)
     assert st in (9, 12)
+
+
+def test_sequence_span_limit():
+    """Kernels address a sequence's rows with 32-bit element offsets: a
+    sequence of L tokens over Hv heads needs L * Hv * 128 < 2^31."""
+    p, keep = _packed([0, 1 << 18], Hqk=64, Hv=64)   # 2^18 * 64 * 128 = 2^31
+    assert _status(kda.kda_fwd_ctx_bytes, p) == 2
+    p, keep = _packed([0, (1 << 18) - 1], Hqk=64, Hv=64)
+    kda.kda_fwd_ctx_bytes(p)
+    p = _fixed(T=1 << 18, Hqk=64, Hv=64)
+    assert _status(kda.kda_fwd_ctx_bytes, p) == 2

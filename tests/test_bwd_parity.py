@@ -18,27 +18,9 @@ from tests import parity_util as pu
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dA_log", "ddt_bias", "dinitial_state")
-
-
-def _run_backward(inp, route=0, ckpt=0):
-    import gated_delta_rule_32_amd as kda
-    o, fs, ctx, d = pu.run_forward(inp, route=route, ckpt=ckpt, save_context=True)
-    grads = kda.recurrent_kda_training_backward(ctx, d.do, d.dfinal_state)
-    torch.cuda.synchronize()
-    return [g.float().cpu().numpy() for g in grads]
-
-
-def _report_and_check(pairs):
-    """pairs: list of (name, got, ref). Prints every error, then asserts."""
-    rows = []
-    for name, x, r in pairs:
-        viol, fr, mx = pu.errors(x, r)
-        rows.append((name, viol, fr, mx))
-        print(f"  {name:16s} worst ratio {viol:.3g}  rel-frob {fr:.3g}  max-abs {mx:.3g}", flush=True)
-    for name, viol, fr, mx in rows:
-        assert viol <= 1.0, f"{name}: elementwise bar exceeded (worst ratio {viol:.3g}, max abs {mx:.3g})"
-        assert fr <= pu.FROB, f"{name}: relative Frobenius error {fr:.3g} > {pu.FROB}"
+NAMES = pu.GRAD_NAMES
+_run_backward = pu.run_backward
+_report_and_check = pu.report_and_check
 
 
 def _small_cases():
