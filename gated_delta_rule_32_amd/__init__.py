@@ -35,7 +35,7 @@ ROUTE_AUTO, ROUTE_CHUNK, ROUTE_ROWSPLIT = 0, 1, 2
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"libkda.so not found at {LIB_PATH}; build it with "
-        "`python -m gated_delta_rule_32_amd.build_lib` (hipcc, gfx950)")
+        "`python gated_delta_rule_32_amd/build_lib.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
