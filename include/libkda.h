@@ -78,7 +78,7 @@ typedef enum {
 } kda_status;
 
 typedef enum {
-    KDA_ROUTE_AUTO = 0,      /* library chooses */
+    KDA_ROUTE_AUTO = 0,      /* library chooses (currently always the chunked kernel) */
     KDA_ROUTE_CHUNK = 1,     /* chunked MFMA kernel */
     KDA_ROUTE_ROWSPLIT = 2   /* per-token FP32 kernel, state rows split across workgroups */
 } kda_route;

@@ -110,8 +110,10 @@ def test_longest_first_order():
 
 
 def test_route_choice():
-    assert kda.kda_plan_query(_fixed())[0] == kda.ROUTE_ROWSPLIT
+    # the chunked kernel is chosen at every task count; the row-split one on request
+    assert kda.kda_plan_query(_fixed())[0] == kda.ROUTE_CHUNK
     assert kda.kda_plan_query(kda.make_problem(8, 64, 16, 16, 8))[0] == kda.ROUTE_CHUNK
+    assert kda.kda_plan_query(_fixed(route=2))[0] == kda.ROUTE_ROWSPLIT
     assert kda.kda_plan_query(_fixed(route=1))[0] == kda.ROUTE_CHUNK
 
 

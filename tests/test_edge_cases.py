@@ -7,7 +7,7 @@ C ABI, forward and backward against the FP64 oracle:
 * beta -> 1 (the delta rule recalls v exactly) and beta -> 0 (pure decay);
 * zero values and zero initial state (output and final state exactly zero);
 * eight value heads per q/k head;
-* one long sequence, which takes the row-split route;
+* one long sequence (a single task) on both routes;
 * sequence lengths on and around the tape interval.
 
 Inputs are the seeded draws of the workload generator with the named tensors
@@ -83,21 +83,17 @@ def test_backward_edge(case, route):
     pu.report_and_check(list(zip(pu.GRAD_NAMES, got, ref)))
 
 
-def test_long_sequence_takes_rowsplit_route():
-    """One 4096-token sequence and one head: too few tasks for the chunked
-    kernel, so the automatic route is the row-split forward."""
-    import gated_delta_rule_32_amd as kda
+@pytest.mark.parametrize("route", [1, 2], ids=["chunk", "rowsplit"])
+def test_long_single_sequence(route):
+    """One 4096-token sequence and one head: a single task, 256 chunks in
+    sequence on the chunked route, 4096 steps on the row-split route."""
     problem = P([4096], 1, 1, packed=True)
     inp = workloads.make_inputs(problem, 208, with_adjoints=True)
-    d = inp.to("cuda")
-    prob = kda.make_problem(1, problem.T, 1, 1, 1, d.cu_seqlens, inp.cu_seqlens)
-    route, _, _ = kda.kda_plan_query(prob)
-    assert route == 2
-    print("[edge] long sequence, automatic route", flush=True)
-    o, fs, _, _ = pu.run_forward(inp, route=0, save_context=False)
+    print(f"[edge] long single sequence, route {route}", flush=True)
+    o, fs, _, _ = pu.run_forward(inp, route=route, save_context=False)
     ref_o, ref_s = pu.oracle_forward(inp)
     pu.assert_close("o", o.float().cpu().numpy(), ref_o)
     pu.assert_state_close("final_state", fs.cpu().numpy(), ref_s)
-    got = pu.run_backward(inp, route=0)
+    got = pu.run_backward(inp, route=route)
     ref = pu.oracle_backward(inp)
     pu.report_and_check(list(zip(pu.GRAD_NAMES, got, ref)))
