@@ -79,19 +79,25 @@ struct BwdLds {
     alignas(16) f32x4 part[4][3][2][64];
 };
 
-__device__ __forceinline__ float xor_sum_gq(float x) {  // sum over the 4 lane rows (gq)
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
+// Sum over the 4 lane rows (gq) of a wave, broadcast to all rows.  A swap of
+// rows 2p <-> 2p+1 (then of halves) returns each lane's own value in one
+// result and its partner's in the other, so their sum is the pair sum.
+__device__ __forceinline__ float xor_sum_gq(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Inclusive suffix sum over the 16 lanes of each row (lane c gets sum of
-// lanes c..15 of its row): DPP row shifts toward lower lanes, zero-filled.
+// lanes c..15 of its row): DPP row shifts toward lower lanes, zero-filled
+// (bound_ctrl: a lane with no source reads 0, which also lets the compiler
+// fold each shift into its add).
 __device__ __forceinline__ float row16_suffix(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x101, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x102, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x104, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x108, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x101, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x102, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x104, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x108, 0xF, 0xF, true));
     return x;
 }
 

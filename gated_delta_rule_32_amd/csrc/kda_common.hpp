@@ -120,12 +120,14 @@ __device__ __forceinline__ f32x4 transpose_frag(bf16x4 x, bf16x4 ident) {
 }
 
 // Sum over each row of 16 lanes, broadcast to the row, with DPP lane swaps
-// (xor 1, xor 2 inside quads, then mirrors of 8 and 16 lanes).
+// (xor 1, xor 2 inside quads, then mirrors of 8 and 16 lanes).  Every lane has
+// a source in these patterns, so bound_ctrl changes nothing here; set, it lets
+// the compiler fold each swap into its add (v_add_f32_dpp).
 __device__ __forceinline__ float row16_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));
     return x;
 }
 
