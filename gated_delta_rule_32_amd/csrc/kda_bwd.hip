@@ -206,10 +206,10 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         const int64_t rec = (rec0 + ci) * a.Hv + h;
         const int kb0 = 2 * wave;
 
-        // Global operands of the state-side products, issued before the
-        // prologue so that their latency hides behind it: this wave's
-        // chunk-start state frags, RF(U) and RF(dO) (zero past the end);
-        // S0 and dO stay in registers until the state update.
+        // Global operands of the state-side products, issued in the prologue
+        // so that their latency hides behind it: this wave's chunk-start
+        // state frags, RF(U) and RF(dO) (zero past the end); S0 and dO stay
+        // in registers until the state update.
         const unsigned tc = (unsigned)(t0 + (kTail ? min(cl, nv - 1) : cl));  // RF row token
         const unsigned ov = __umul24(tc, sv), oq = __umul24(tc, sq);          // its row offsets
         // the chunk's T^T, Akk^T, Aqk' record first (its LDS copy is made at
@@ -217,18 +217,6 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         float4 ta4 = make_float4(0.f, 0.f, 0.f, 0.f);
         if (tix < REC_TA / 4) ta4 = *(const float4*)at(a.rec_ta + rec * REC_TA, 4 * tix);
         bf16x4 s0f[8][2], ru[8], rdo[8];
-        {
-            const bf16* up = (const bf16*)a.rec_u + rec * REC_U;      // uniform record bases
-            const bf16* s0p = (const bf16*)a.rec_s0 + rec * REC_S0;
-#pragma unroll
-            for (int vb = 0; vb < 8; ++vb) {
-                ru[vb] = *(const bf16x4*)at(up, vb * 256 + lane * 4);
-                rdo[vb] = *(const bf16x4*)at(dop0, ov + 16 * vb + 4 * gq);
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    s0f[vb][j] = *(const bf16x4*)at(s0p, ((kb0 + j) * 8 + vb) * 256 + lane * 4);
-            }
-        }
 
         // ---- P1: norms, gate, beta (row-owner mapping); stage T, Akk, Aqk ----
         {
@@ -257,6 +245,17 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 sm.rkn[r] = valid_r ? fast_rsqrt(sk + 1e-6f) : 0.f;
             }
         }
+        // The state-side loads are spread over P1 and P2, each batch after
+        // the phase's arithmetic: a wave's loads queue at the memory pipeline
+        // and would otherwise hold back the in-order issue of that work.
+        {
+            const bf16* s0p = (const bf16*)a.rec_s0 + rec * REC_S0;  // uniform record base
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    s0f[vb][j] = *(const bf16x4*)at(s0p, ((kb0 + j) * 8 + vb) * 256 + lane * 4);
+        }
         __syncthreads();
         // ---- P2: prefix sums over the chunk's tokens ----
         if (tix < D) {
@@ -267,6 +266,14 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 sm.lam[rr][tix] = acc;
             }
             sm.gamc[tix] = __builtin_amdgcn_exp2f(acc);
+        }
+        {
+            const bf16* up = (const bf16*)a.rec_u + rec * REC_U;
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb) {
+                ru[vb] = *(const bf16x4*)at(up, vb * 256 + lane * 4);
+                rdo[vb] = *(const bf16x4*)at(dop0, ov + 16 * vb + 4 * gq);
+            }
         }
         __syncthreads();
         // ---- P3: the chunk's operands into LDS ----
