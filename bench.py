@@ -253,9 +253,52 @@ def main():
                       "frac_of_hbm_peak": round(ab / (bwd_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "kernels": ["fwd_chunk_kernel<rebuild>", "bwd_chunk_kernel",
                                   "bwd_param_reduce_kernel", "bwd_dqk_reduce_kernel"]}
+        if route == 1:
+            out["records_context"] = records_context_step(kda, p, d, inp_cpu, args, stream)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp_cpu)
     print(json.dumps(out), flush=True)
+
+
+def records_context_step(kda, p, d, inp_cpu, args, stream):
+    """The same training step with the per-chunk records context: the forward
+    stores every chunk's records and the backward reruns no forward
+    recurrence.  Timed like the main step (HIP events on the kernels' stream)."""
+    import torch
+    prob = kda.make_problem(p.B, p.T, p.Hqk, p.Hv, p.N, d.cu_seqlens, inp_cpu.cu_seqlens,
+                            route=args.route, context=kda.CONTEXT_RECORDS)
+    ctx_bytes = kda.kda_fwd_ctx_bytes(prob)
+    ctx = torch.empty(ctx_bytes, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(kda.kda_bwd_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(d.v)
+    fs = torch.empty_like(d.initial_state)
+    grads = (torch.empty_like(d.q), torch.empty_like(d.k), torch.empty_like(d.v),
+             torch.empty_like(d.g), torch.empty_like(d.beta), torch.empty_like(d.A_log),
+             torch.empty_like(d.dt_bias), torch.empty_like(d.initial_state))
+    h = stream.cuda_stream
+
+    def step():
+        kda.kda_fwd(prob, d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
+                    o, fs, ctx, h)
+        e1.record(stream)
+        kda.kda_bwd(prob, d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
+                    ctx, d.do, d.dfinal_state, *grads, ws, h)
+
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for _ in range(max(args.warmup, 2)):
+        step()
+    torch.cuda.synchronize()
+    fwd, bwd = [], []
+    for _ in range(args.steps):
+        e0.record(stream)
+        step()
+        e2.record(stream)
+        torch.cuda.synchronize()
+        fwd.append(e0.elapsed_time(e1))
+        bwd.append(e1.elapsed_time(e2))
+    fm, bm = sum(fwd) / len(fwd), sum(bwd) / len(bwd)
+    return {"fwd_ms_mean": round(fm, 4), "bwd_ms_mean": round(bm, 4), "step_ms": round(fm + bm, 4),
+            "ctx_bytes": ctx_bytes}
 
 
 if __name__ == "__main__":

@@ -52,6 +52,7 @@ struct Prob {
     bool packed;
     int route;      // resolved: 1 chunk, 2 rowsplit
     int ck;         // tape interval
+    int ctxmode;    // KDA_CONTEXT_TAPE or KDA_CONTEXT_RECORDS
     float scale;
     std::vector<int64_t> len;    // per sequence
     std::vector<int64_t> start;  // flattened token offset per sequence
@@ -97,12 +98,17 @@ kda_status validate(const kda_problem* p, Prob& out) {
     if (ck <= 0 || ck % kChunk != 0)
         return fail(KDA_ERR_ROUTE, "checkpoint_every must be a positive multiple of 16 (got %d)",
                     p->checkpoint_every);
+    if (p->context != KDA_CONTEXT_TAPE && p->context != KDA_CONTEXT_RECORDS)
+        return fail(KDA_ERR_ROUTE, "unknown context kind %d", p->context);
+    if (p->context == KDA_CONTEXT_RECORDS && p->route == 2)
+        return fail(KDA_ERR_ROUTE, "per-chunk records need the chunked route");
 
     out = Prob{};
     out.B = p->B; out.T = p->T; out.Hqk = p->Hqk; out.Hv = p->Hv; out.N = p->N;
     out.G = p->Hv / p->Hqk;
     out.packed = packed;
     out.ck = ck;
+    out.ctxmode = p->context;
     out.scale = want_scale;
     out.tokens = (int64_t)p->B * p->T;
     if (packed) {
@@ -263,7 +269,7 @@ kda::DevPlan dev_plan(const PlanEntry* e) {
 // ---------------------------------------------------------------------------
 struct CtxRecord {
     std::vector<int64_t> key;   // plan key (device, Hv, ck, layout, lengths)
-    int B, T, Hqk, Hv, N, route;
+    int B, T, Hqk, Hv, N, route, ctxmode;
     const void* ptrs[8];
     hipStream_t stream;
     size_t ctx_bytes;
@@ -273,7 +279,26 @@ std::map<const void*, CtxRecord> g_ctx;
 size_t tape_bytes(const Prob& p) {
     return (size_t)p.total_ck * (size_t)p.Hv * (size_t)kStateElems * sizeof(float);
 }
-size_t ctx_bytes_for(const Prob& p) { return 256 + tape_bytes(p); }
+// per (16-token chunk, value head) record: BF16 chunk-start state frags,
+// BF16 RF(U), FP32 T^T, Akk^T and scale*Aqk
+constexpr size_t kRecS0 = (size_t)kStateElems * 2, kRecU = (size_t)kChunk * D * 2,
+                 kRecTA = (size_t)3 * kChunk * kChunk * sizeof(float);
+struct RecLayout {
+    size_t s0, u, ta, end;  // byte offsets of the three record arrays
+};
+RecLayout rec_layout(size_t recs, size_t base) {
+    RecLayout r;
+    r.s0 = base;
+    r.u = align256(r.s0 + recs * kRecS0);
+    r.ta = align256(r.u + recs * kRecU);
+    r.end = align256(r.ta + recs * kRecTA);
+    return r;
+}
+size_t ctx_bytes_for(const Prob& p) {
+    if (p.ctxmode == KDA_CONTEXT_RECORDS)
+        return rec_layout((size_t)p.total_chunks * p.Hv, 256).end;
+    return 256 + tape_bytes(p);
+}
 
 struct Span {
     const void* p;
@@ -371,11 +396,13 @@ struct WsLayout {
 };
 static WsLayout ws_layout(const Prob& p) {
     WsLayout w;
-    const size_t recs = (size_t)p.total_chunks * p.Hv;
-    size_t off = 0;
-    w.s0 = off;  off = align256(off + recs * kStateElems * 2);
-    w.u = off;   off = align256(off + recs * kChunk * D * 2);
-    w.ta = off;  off = align256(off + recs * 3 * kChunk * kChunk * sizeof(float));
+    // the rebuilt chunk records (none when the context already holds them)
+    const size_t recs = p.ctxmode == KDA_CONTEXT_RECORDS ? 0 : (size_t)p.total_chunks * p.Hv;
+    const RecLayout r = rec_layout(recs, 0);
+    w.s0 = r.s0;
+    w.u = r.u;
+    w.ta = r.ta;
+    size_t off = r.end;
     w.dqk = off;
     if (p.G > 1) off = align256(off + (size_t)p.tokens * p.Hv * 2 * D * sizeof(float));
     w.par = off;
@@ -440,13 +467,22 @@ kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const vo
     kda::FwdArgs a = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, initial_state);
     a.o = o;
     a.s_final = final_state;
-    a.tape = ctx ? (float*)((char*)ctx + 256) : nullptr;
+    a.tape = nullptr;
+    if (ctx != nullptr && p.ctxmode == KDA_CONTEXT_RECORDS) {
+        const RecLayout r = rec_layout((size_t)p.total_chunks * p.Hv, 256);
+        a.rec_s0 = (kda::bf16_t*)((char*)ctx + r.s0);
+        a.rec_u = (kda::bf16_t*)((char*)ctx + r.u);
+        a.rec_ta = (float*)((char*)ctx + r.ta);
+    } else if (ctx != nullptr) {
+        a.tape = (float*)((char*)ctx + 256);
+    }
     e = (p.route == 1) ? kda::launch_fwd_chunk(a, stream) : kda::launch_fwd_rowsplit(a, stream);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     if (ctx != nullptr) {
         CtxRecord r;
         r.key = plan_key(p, dev);
         r.B = p.B; r.T = p.T; r.Hqk = p.Hqk; r.Hv = p.Hv; r.N = p.N; r.route = p.route;
+        r.ctxmode = p.ctxmode;
         const void* ptrs[8] = {q, k, v, g, beta, A_log, dt_bias, initial_state};
         std::memcpy(r.ptrs, ptrs, sizeof(ptrs));
         r.stream = stream;
@@ -488,7 +524,7 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
         const CtxRecord& r = it->second;
         const void* ptrs[8] = {q, k, v, g, beta, A_log, dt_bias, initial_state};
         if (r.key != plan_key(p, dev) || r.B != p.B || r.T != p.T || r.Hqk != p.Hqk ||
-            r.Hv != p.Hv || r.N != p.N)
+            r.Hv != p.Hv || r.N != p.N || r.ctxmode != p.ctxmode)
             return fail(KDA_ERR_CTX_MISMATCH, "context was made for another shape or device");
         if (std::memcmp(r.ptrs, ptrs, sizeof(ptrs)) != 0)
             return fail(KDA_ERR_CTX_MISMATCH, "inputs differ from the forward that made the context");
@@ -518,11 +554,19 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
 
     kda::BwdArgs b{};
     b.f = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, initial_state);
-    b.f.tape = (float*)((char*)ctx + 256);
     char* ws = (char*)workspace;
-    b.f.rec_s0 = (kda::bf16_t*)(ws + wl.s0);
-    b.f.rec_u = (kda::bf16_t*)(ws + wl.u);
-    b.f.rec_ta = (float*)(ws + wl.ta);
+    const bool records = p.ctxmode == KDA_CONTEXT_RECORDS;
+    if (records) {  // the forward stored every chunk's records in the context
+        const RecLayout r = rec_layout((size_t)p.total_chunks * p.Hv, 256);
+        b.f.rec_s0 = (kda::bf16_t*)((char*)ctx + r.s0);
+        b.f.rec_u = (kda::bf16_t*)((char*)ctx + r.u);
+        b.f.rec_ta = (float*)((char*)ctx + r.ta);
+    } else {        // rebuilt from the tape into the workspace
+        b.f.tape = (float*)((char*)ctx + 256);
+        b.f.rec_s0 = (kda::bf16_t*)(ws + wl.s0);
+        b.f.rec_u = (kda::bf16_t*)(ws + wl.u);
+        b.f.rec_ta = (float*)(ws + wl.ta);
+    }
     b.d_o = d_o; b.dfinal = dfinal_state;
     b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg; b.dbeta = dbeta;
     b.dA_log = dA_log; b.ddt_bias = ddt_bias; b.dinit = dinitial_state;
@@ -530,11 +574,13 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
     b.dparam_part = (float*)(ws + wl.par);
     b.total_tokens = p.tokens;
 
-    // segment list sits after the chunk offsets in the schedule
-    kda::FwdArgs rb = b.f;
-    rb.plan.task = (const int32_t*)((const char*)plan->dev + plan->off_seg);
-    e = kda::launch_state_rebuild(rb, p.total_segs * p.Hv, stream);
-    if (e != hipSuccess) return hip_fail(e, "state rebuild launch");
+    if (!records) {
+        // segment list sits after the chunk offsets in the schedule
+        kda::FwdArgs rb = b.f;
+        rb.plan.task = (const int32_t*)((const char*)plan->dev + plan->off_seg);
+        e = kda::launch_state_rebuild(rb, p.total_segs * p.Hv, stream);
+        if (e != hipSuccess) return hip_fail(e, "state rebuild launch");
+    }
     e = kda::launch_bwd_chunk(b, stream);
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     e = kda::launch_bwd_reduce(b, p.N, stream);

@@ -115,13 +115,20 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], 
 
 }  // namespace
 
-// kRebuild = false: the training forward over whole tasks (o, final state,
-// tape).  kRebuild = true: the backward's state rebuild over one tape segment
-// of one task: it starts from the segment's checkpoint, writes no output, and
-// stores for every chunk the records the adjoint reads (chunk-start state, U,
-// T, Akk, Aqk).
-template <bool kRebuild>
+// kMode = kFwdTape: the training forward over whole tasks (o, final state, the
+// FP32 state tape).  kMode = kFwdRebuild: the backward's state rebuild over one
+// tape segment of one task: it starts from the segment's checkpoint, writes no
+// output, and stores for every chunk the records the adjoint reads
+// (chunk-start state, U, T, Akk, Aqk).  kMode = kFwdRecords: the training
+// forward that stores those records for every chunk instead of the tape, so
+// that the backward reruns nothing.
+constexpr int kFwdTape = 0, kFwdRebuild = 1, kFwdRecords = 2;
+
+template <int kMode>
 __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
+    constexpr bool kRebuild = kMode == kFwdRebuild;  // one segment, no output
+    constexpr bool kOut = kMode != kFwdRebuild;      // o and the final state
+    constexpr bool kRec = kMode != kFwdTape;         // per-chunk records
     __shared__ FwdLds sm;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -153,8 +160,8 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         cb = seg * per;
         ce = min(cb + per, nchunks);
         if (seg > 0) src = a.tape + ((tape_base + seg - 1) * a.Hv + h) * (int64_t)D * D;
-        rec0 = a.plan.chunk_off[n];
     }
+    if constexpr (kRec) rec0 = a.plan.chunk_off[n];
 
     // state: S^T frags for kb = 0..7 and vb = 2*wave + {0, 1}
     f32x4 S[8][2];
@@ -359,7 +366,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                     const bf16x4 s1 = to_bf4(S[2 * j + 1][vb]);
                     sb[j][vb] = cat8(s0, s1);
                     Y[vb] = mma32(kg8, sb[j][vb], Y[vb]);    // lane (gq, v) holds Y[4gq+i][v]
-                    if constexpr (kRebuild) {
+                    if constexpr (kRec) {
                         // chunk-start state record: frag (kb, vb) with lane (gq, k)
                         // holding S0[16vb + 4gq + i][16kb + k]
                         const bf16x4 ident = identity_frag(lane);
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                     }
                 }
             }
-            if constexpr (!kRebuild) {
+            if constexpr (kOut) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const bf16x8 q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
@@ -397,7 +404,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             col.z = (cl < 4 * gq + 2) ? b4.z * akk[2] : 0.f;
             col.w = (cl < 4 * gq + 3) ? b4.w * akk[3] : 0.f;
             *(float4*)&ws.nT[cl][4 * gq] = col;
-            if (kRebuild) {
+            if constexpr (kRec) {
                 // Akk^T[col][row] = Akk[row][col] for row > col
                 float4 m;
                 m.x = (cl < 4 * gq + 0) ? akk[0] : 0.f;
@@ -430,7 +437,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 if (m < 14) y[2] -= nm.z * tm;
                 y[3] -= nm.w * tm;
             }
-            if (kRebuild)   // T^T[col][row]
+            if constexpr (kRec)   // T^T[col][row]
                 *(float4*)at(a.rec_ta + rec * 768, colx * 16 + 4 * qd) = make_float4(y[0], y[1], y[2], y[3]);
             // Tb[i][col] = T[i][col] beta_col
             const float bc = sm.beta[ci & 1][colx];
@@ -450,9 +457,9 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             f32x4 am;
 #pragma unroll
             for (int i = 0; i < 4; ++i) am[i] = (4 * gq + i <= cl) ? aqkT[i] : 0.f;
-            if constexpr (kRebuild)   // Aqk[row = cl][col = 4gq + i], scale included
+            if constexpr (kRec)   // Aqk[row = cl][col = 4gq + i], scale included
                 *(float4*)at(a.rec_ta + rec * 768, 512 + cl * 16 + 4 * gq) = make_float4(am[0], am[1], am[2], am[3]);
-            else
+            if constexpr (kOut)
                 *(bf16x4*)&sm.sh_aq[lane * 4] = to_bf4(am);
             phase_a(ci + 1, rq_next, rk_next);
         } else {
@@ -469,7 +476,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             split4(f32x4{t4.x, t4.y, t4.z, t4.w}, tbh, tbl);
         }
         bf16x4 aq;
-        if constexpr (!kRebuild) aq = ld4(&sm.sh_aq[0], lane);
+        if constexpr (kOut) aq = ld4(&sm.sh_aq[0], lane);
         // CF(V) for the wave's columns (RF(V) times the identity, exact), then
         // U = Tb V - Tb Y
         f32x4 U[2];
@@ -494,12 +501,12 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
         for (int vb = 0; vb < 2; ++vb) {
             split4(U[vb], uh[vb], ul[vb]);
-            if constexpr (kRebuild) {
+            if constexpr (kRec) {
                 // U record, RF layout: lane (gq, c) holds U[c][16vb + 4gq + i]
                 const bf16x4 ut = to_bf4(transpose_frag(to_bf4(U[vb]), identity_frag(lane)));
                 *(bf16x4*)at((bf16*)a.rec_u + rec * (CH * D), ((2 * wave + vb) * 64 + lane) * 4) = ut;
-                continue;
             }
+            if constexpr (!kOut) continue;
             // the chain's last step is a 16x16x32 as well (upper half zero)
             OT[vb] = mma32(cat8(uh[vb], zb), cat8(aq, zb), OT[vb]);
             // lane (gq, c) holds O[c][32w + 16vb + 4gq + i]
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             }
         }
         const int tend = t0 + nv;
-        if (!kRebuild && a.tape != nullptr && tend < L && (tend % a.ck_every) == 0) {
+        if (kMode == kFwdTape && a.tape != nullptr && tend < L && (tend % a.ck_every) == 0) {
             const int64_t jck = tend / a.ck_every;
             store_state(a.tape + ((tape_base + jck - 1) * a.Hv + h) * (int64_t)D * D, S, wave, gq, cl);
         }
@@ -538,20 +545,25 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     const int cfull = min(ce, nfull);
     for (int ci = cb; ci < cfull; ++ci) chunk(ci, std::false_type{});
     if (nfull < ce) chunk(nfull, std::true_type{});
-    if (!kRebuild && a.s_final != nullptr)
+    if (kOut && a.s_final != nullptr)
         store_state(a.s_final + slab, S, wave, (tid & 63) >> 4, tid & 15);
 }
 
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s) {
     if (a.num_tasks == 0) return hipSuccess;
-    hipLaunchKernelGGL(fwd_chunk_kernel<false>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0, s, a);
+    if (a.rec_s0 != nullptr)
+        hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRecords>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL(fwd_chunk_kernel<kFwdTape>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0, s,
+                           a);
     return hipGetLastError();
 }
 
 // One workgroup per (tape segment, value head): num_items = segments * Hv.
 hipError_t launch_state_rebuild(const FwdArgs& a, int64_t num_items, hipStream_t s) {
     if (num_items == 0) return hipSuccess;
-    hipLaunchKernelGGL(fwd_chunk_kernel<true>, dim3((unsigned)num_items), dim3(FC_THREADS), 0, s, a);
+    hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRebuild>, dim3((unsigned)num_items), dim3(FC_THREADS), 0, s, a);
     return hipGetLastError();
 }
 

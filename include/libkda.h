@@ -83,6 +83,19 @@ typedef enum {
     KDA_ROUTE_ROWSPLIT = 2   /* per-token FP32 kernel, state rows split across workgroups */
 } kda_route;
 
+/* What the training forward saves for the backward.  TAPE: the FP32 state
+ * every checkpoint_every tokens; the backward rebuilds each segment's chunk
+ * states from it (small context, a rebuild pass in the backward).  RECORDS:
+ * every chunk's start state (BF16), U (BF16) and T, Akk, Aqk (FP32), about
+ * 39 KiB per 16 tokens and value head; the backward reruns no forward
+ * recurrence (page "flashinfer.kda_training", paragraph 5), at the cost of a
+ * larger context and a forward that writes it.  RECORDS needs the chunked
+ * route. */
+typedef enum {
+    KDA_CONTEXT_TAPE = 0,
+    KDA_CONTEXT_RECORDS = 1
+} kda_context;
+
 /* One call's shape.  All fields are read by value; the struct is not kept. */
 typedef struct {
     int32_t B;                       /* physical batch (1 when packed) */
@@ -96,6 +109,7 @@ typedef struct {
     float lower_bound;               /* must be -5 */
     int32_t route;                   /* kda_route; AUTO unless testing a route */
     int32_t checkpoint_every;        /* tape interval in tokens; 0 selects 256; a multiple of 16 */
+    int32_t context;                 /* kda_context: what the forward saves for the backward */
 } kda_problem;
 
 /* Library version (KDA_VERSION). */
@@ -107,13 +121,15 @@ const char* kda_status_string(kda_status status);
 /* Text of the last failure on this thread ("" if none). */
 const char* kda_last_error(void);
 
-/* Bytes the forward context needs: the FP32 state tape saved for the
- * backward (one [Hv][128][128] slab per sequence and per interval boundary
- * strictly inside the sequence) plus alignment.  Validates the problem. */
+/* Bytes the forward context needs: with KDA_CONTEXT_TAPE the FP32 state tape
+ * saved for the backward (one [Hv][128][128] slab per sequence and per
+ * interval boundary strictly inside the sequence), with KDA_CONTEXT_RECORDS
+ * one record per 16-token chunk and value head; plus alignment.  Validates
+ * the problem. */
 kda_status kda_fwd_ctx_bytes(const kda_problem* p, size_t* bytes);
 
-/* Bytes the backward workspace needs (chunk-start states rebuilt from the
- * tape, FP32 partial sums).  Validates the problem. */
+/* Bytes the backward workspace needs (with KDA_CONTEXT_TAPE the chunk
+ * records rebuilt from the tape; FP32 partial sums).  Validates the problem. */
 kda_status kda_bwd_workspace_bytes(const kda_problem* p, size_t* bytes);
 
 /* Host planning only (no device access): the route the forward would take,

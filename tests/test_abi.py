@@ -164,3 +164,26 @@ def test_sequence_span_limit():
     kda.kda_fwd_ctx_bytes(p)
     p = _fixed(T=1 << 18, Hqk=64, Hv=64)
     assert _status(kda.kda_fwd_ctx_bytes, p) == 2
+
+
+def test_records_context_sizes_and_rejections():
+    """Per-chunk records context: one record per (16-token chunk, value head),
+    laid out as three arrays after a 256-byte header; the backward workspace
+    then holds no records."""
+    cu = [0, 300, 301, 812]
+    p, keep = _packed(cu, Hqk=1, Hv=2)
+    ws_tape = kda.kda_bwd_workspace_bytes(p)
+    p.context = kda.CONTEXT_RECORDS
+    chunks = sum((L + 15) // 16 for L in (300, 1, 511))
+    recs = chunks * 2
+    ctx = kda.kda_fwd_ctx_bytes(p)
+    need = 256 + recs * (128 * 128 * 2 + 16 * 128 * 2 + 3 * 16 * 16 * 4)
+    assert need <= ctx <= need + 3 * 256
+    ws_rec = kda.kda_bwd_workspace_bytes(p)
+    rec_bytes = recs * (128 * 128 * 2 + 16 * 128 * 2 + 3 * 16 * 16 * 4)
+    assert ws_rec + rec_bytes <= ws_tape <= ws_rec + rec_bytes + 3 * 256
+    p.route = 2
+    assert _status(kda.kda_fwd_ctx_bytes, p) == 11      # records need the chunked route
+    p.route = 0
+    p.context = 5
+    assert _status(kda.kda_fwd_ctx_bytes, p) == 11      # unknown context kind
