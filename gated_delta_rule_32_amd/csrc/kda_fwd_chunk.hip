@@ -21,10 +21,11 @@
 // Work split.  One workgroup (4 waves) owns one (sequence, value head) task
 // for its whole length; wave w owns state columns v in [32w, 32w+32), held as
 // transposed 16x16 frags S^T[kb][vb] in FP32 registers.  The state path is
-// column-local, so no state crosses waves.  Four barriers per chunk: after
-// the gate (the prefix sums need every row), after the prefix sums, after the
-// chunk's shared operands are in LDS, and after the chunk's 16x16 algebra
-// (Akk and the substitution on wave 0, Aqk on wave 1, shared through LDS).
+// column-local, so no state crosses waves.  Three barriers per chunk: at its
+// start (its decay prefix sums, exp(gC) and beta are in LDS), after its shared
+// operands are in LDS, and after its 16x16 algebra (Akk and the substitution
+// on wave 0, Aqk on wave 1, shared through LDS).  The next chunk's norms and
+// gate run inside the algebra phase, its prefix sums inside the state update.
 // Shared operands sit in LDS "frag slots" (64 lanes x 4 bf16, padded):
 //   RF(X)[kb]: lane (gq, c) holds X[c][16kb + 4gq + i]   (rows = tokens)
 //   CF(X)[kb]: lane (gq, k) holds X[4gq + i][16kb + k]   (tokens along i)
@@ -487,12 +488,14 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             const bf16x4 ident = to_bf4(id);
             const bf16x4 cfv0 = to_bf4(mma16(vcur.v0, ident, zero4()));
             const bf16x4 cfv1 = to_bf4(mma16(vcur.v1, ident, zero4()));
-            U[0] = mma16(tbh, cfv0, zero4());
-            U[0] = mma16(tbl, cfv0, U[0]);
-            U[0] = mma16(tbh, to_bf4_neg(Y[0]), U[0]);
-            U[1] = mma16(tbh, cfv1, zero4());
-            U[1] = mma16(tbl, cfv1, U[1]);
-            U[1] = mma16(tbh, to_bf4_neg(Y[1]), U[1]);
+            // a 16x16x32 costs about what a 16x16x16 does, so the three K=16
+            // products take two: [Tb_hi|Tb_lo] [V;V] and [Tb_hi|Tb_lo] [-Y;0]
+            const bf16x8 tb2 = cat8(tbh, tbl);
+            const bf16x4 zb = to_bf4(zero4());
+            U[0] = mma32(tb2, cat8(cfv0, cfv0), zero4());
+            U[0] = mma32(tb2, cat8(to_bf4_neg(Y[0]), zb), U[0]);
+            U[1] = mma32(tb2, cat8(cfv1, cfv1), zero4());
+            U[1] = mma32(tb2, cat8(to_bf4_neg(Y[1]), zb), U[1]);
         }
         load_cols_s(vcur, sp, min(t0 + CH + cl, L - 1), 32 * wave + 4 * gq);
         // O^T += U^T Aqk^T, store; then S update
@@ -516,21 +519,27 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             }
         }
         phase_b(ci + 1);
-        // (one accumulation chain keeps one MFMA shape: a 16x16x16 that reads
-        // the accumulator of a 16x16x32 issued just before it has been seen
-        // to miss that product)
+        // S^T += Kt^T U with the three hi/lo products in two 16x16x32s:
+        // [Kt_hi|Kt_lo] [U_hi;U_hi] and [Kt_hi|Kt_lo] [U_lo;0].  (One
+        // accumulation chain keeps one MFMA shape: a 16x16x16 that reads the
+        // accumulator of a 16x16x32 issued just before it has been seen to
+        // miss that product.)
+        bf16x8 uu[2], u0[2];
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb) {
+            uu[vb] = cat8(uh[vb], uh[vb]);
+            u0[vb] = cat8(ul[vb], zb);
+        }
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-            const bf16x4 th = ld4(&sm.cf_kth[kb * FS], lane);
-            const bf16x4 tl = ld4(&sm.cf_ktl[kb * FS], lane);
+            const bf16x8 t2 = cat8(ld4(&sm.cf_kth[kb * FS], lane), ld4(&sm.cf_ktl[kb * FS], lane));
             const float4 gd = *(const float4*)&sm.gamc[ci & 1][16 * kb + 4 * gq];
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb) {
                 f32x4 s = S[kb][vb];
                 s[0] *= gd.x; s[1] *= gd.y; s[2] *= gd.z; s[3] *= gd.w;
-                s = mma16(th, uh[vb], s);
-                s = mma16(th, ul[vb], s);
-                s = mma16(tl, uh[vb], s);
+                s = mma32(t2, uu[vb], s);
+                s = mma32(t2, u0[vb], s);
                 S[kb][vb] = s;
             }
         }
