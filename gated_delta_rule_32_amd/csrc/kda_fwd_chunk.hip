@@ -51,6 +51,7 @@ namespace {
 
 constexpr int FC_THREADS = 256;
 constexpr int TBS = 20;  // row stride of the per-wave Tb scratch (16-byte rows)
+constexpr int FS2 = 520;  // stride of a slot that holds 8 bf16 per lane (512 + 8 padding)
 
 struct SolveScratch {
     alignas(16) float nT[CH][CH];   // nT[m][i] = beta_i Akk[i][m] for i > m, else 0 (wave 0 only)
@@ -64,12 +65,11 @@ struct FwdLds {
     alignas(16) float beta[2][CH];  // double-buffered: a wave may start the next
                                     // chunk while another still solves with this one's
     SolveScratch sv;
-    alignas(16) bf16 sh_aq[256];    // RF16(Aqk) frag, written by wave 1
+    alignas(16) bf16 sh_aq[512];    // [Aqk/2 | Aqk/2] frag pair (RF16 layout), written by wave 1
     alignas(16) bf16 rf_qg[8 * FS];
     alignas(16) bf16 rf_kg[8 * FS];
     alignas(16) bf16 rf_ki[8 * FS];
-    alignas(16) bf16 cf_kth[8 * FS];
-    alignas(16) bf16 cf_ktl[8 * FS];
+    alignas(16) bf16 cf_kt[8 * FS2];  // CF(Kt) as [hi | lo] pairs, 8 bf16 per lane
 };
 
 struct ColIn {   // V for the wave's 32 columns: RF(V)[2w], RF(V)[2w+1]
@@ -334,15 +334,16 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 *(bf16x4*)&sm.rf_kg[orf + 64 * s] = kg4[s];
                 *(bf16x4*)&sm.rf_ki[orf + 64 * s] = ki4[s];
             }
-            // CF(Kt) hi / lo: channel c8 + j of row r sits 4j elements after
-            // channel c8 (the 8 channels share one 16-channel block)
-            const int ocf = cf_off(r, c8);
+            // CF(Kt) hi / lo pairs: lane slot (gq, k) holds the hi parts of
+            // tokens 4gq..4gq+3, then their lo parts; channel c8 + j of row r
+            // sits 8j elements after channel c8 (one 16-channel block)
+            const int ocf = (c8 >> 4) * FS2 + (((r >> 2) << 4) + (c8 & 15)) * 8 + (r & 3);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                sm.cf_kth[ocf + 4 * j] = th4[0][j];
-                sm.cf_kth[ocf + 4 * (j + 4)] = th4[1][j];
-                sm.cf_ktl[ocf + 4 * j] = tl4[0][j];
-                sm.cf_ktl[ocf + 4 * (j + 4)] = tl4[1][j];
+                sm.cf_kt[ocf + 8 * j] = th4[0][j];
+                sm.cf_kt[ocf + 8 * (j + 4)] = th4[1][j];
+                sm.cf_kt[ocf + 8 * j + 4] = tl4[0][j];
+                sm.cf_kt[ocf + 8 * (j + 4) + 4] = tl4[1][j];
             }
         }
         // the row inputs are dead: fetch the next chunk's into the same registers
@@ -460,8 +461,12 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             for (int i = 0; i < 4; ++i) am[i] = (4 * gq + i <= cl) ? aqkT[i] : 0.f;
             if constexpr (kRec)   // Aqk[row = cl][col = 4gq + i], scale included
                 *(float4*)at(a.rec_ta + rec * 768, 512 + cl * 16 + 4 * gq) = make_float4(am[0], am[1], am[2], am[3]);
-            if constexpr (kOut)
-                *(bf16x4*)&sm.sh_aq[lane * 4] = to_bf4(am);
+            if constexpr (kOut) {
+                // halved and stored twice: [Aqk/2 | Aqk/2] against [U_hi | U_hi]
+                // is U_hi Aqk in one 16x16x32 (halving is exact)
+                const bf16x4 h = to_bf4(am * 0.5f);
+                *(bf16x8*)&sm.sh_aq[lane * 8] = cat8(h, h);
+            }
             phase_a(ci + 1, rq_next, rk_next);
         } else {
             y_ot();
@@ -476,8 +481,8 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             const float4 t4 = *(const float4*)&sm.sv.tb[cl][4 * gq];
             split4(f32x4{t4.x, t4.y, t4.z, t4.w}, tbh, tbl);
         }
-        bf16x4 aq;
-        if constexpr (kOut) aq = ld4(&sm.sh_aq[0], lane);
+        bf16x8 aq2;
+        if constexpr (kOut) aq2 = *(const bf16x8*)&sm.sh_aq[lane * 8];
         // CF(V) for the wave's columns (RF(V) times the identity, exact), then
         // U = Tb V - Tb Y
         f32x4 U[2];
@@ -488,30 +493,32 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             const bf16x4 ident = to_bf4(id);
             const bf16x4 cfv0 = to_bf4(mma16(vcur.v0, ident, zero4()));
             const bf16x4 cfv1 = to_bf4(mma16(vcur.v1, ident, zero4()));
-            // a 16x16x32 costs about what a 16x16x16 does, so the three K=16
-            // products take two: [Tb_hi|Tb_lo] [V;V] and [Tb_hi|Tb_lo] [-Y;0]
+            // a 16x16x32 costs about what a 16x16x16 does, so the hi/lo
+            // products take two: [Tb_hi|Tb_lo] [V;V] and [Tb_hi|Tb_lo] [-Y;-Y]
+            // (every operand tuple is formed where it is produced, no copies)
             const bf16x8 tb2 = cat8(tbh, tbl);
-            const bf16x4 zb = to_bf4(zero4());
             U[0] = mma32(tb2, cat8(cfv0, cfv0), zero4());
-            U[0] = mma32(tb2, cat8(to_bf4_neg(Y[0]), zb), U[0]);
+            U[0] = mma32(tb2, cat8(to_bf4_neg(Y[0]), to_bf4_neg(Y[0])), U[0]);
             U[1] = mma32(tb2, cat8(cfv1, cfv1), zero4());
-            U[1] = mma32(tb2, cat8(to_bf4_neg(Y[1]), zb), U[1]);
+            U[1] = mma32(tb2, cat8(to_bf4_neg(Y[1]), to_bf4_neg(Y[1])), U[1]);
         }
         load_cols_s(vcur, sp, min(t0 + CH + cl, L - 1), 32 * wave + 4 * gq);
-        // O^T += U^T Aqk^T, store; then S update
-        bf16x4 uh[2], ul[2];
-        const bf16x4 zb = to_bf4(zero4());
+        // O^T += U^T Aqk^T, store; then S update.  U as [hi|hi] and [lo|lo]
+        bf16x8 uu[2], ll[2];
 #pragma unroll
         for (int vb = 0; vb < 2; ++vb) {
-            split4(U[vb], uh[vb], ul[vb]);
+            bf16x4 uh, ul;
+            split4(U[vb], uh, ul);
+            uu[vb] = cat8(uh, uh);
+            ll[vb] = cat8(ul, ul);
             if constexpr (kRec) {
                 // U record, RF layout: lane (gq, c) holds U[c][16vb + 4gq + i]
                 const bf16x4 ut = to_bf4(transpose_frag(to_bf4(U[vb]), identity_frag(lane)));
                 *(bf16x4*)at((bf16*)a.rec_u + rec * (CH * D), ((2 * wave + vb) * 64 + lane) * 4) = ut;
             }
             if constexpr (!kOut) continue;
-            // the chain's last step is a 16x16x32 as well (upper half zero)
-            OT[vb] = mma32(cat8(uh[vb], zb), cat8(aq, zb), OT[vb]);
+            // the chain's last step is a 16x16x32 as well
+            OT[vb] = mma32(uu[vb], aq2, OT[vb]);
             // lane (gq, c) holds O[c][32w + 16vb + 4gq + i]
             if (cl < nv) {
                 const bf16x4 ob = to_bf4(OT[vb]);
@@ -519,27 +526,20 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             }
         }
         phase_b(ci + 1);
-        // S^T += Kt^T U with the three hi/lo products in two 16x16x32s:
-        // [Kt_hi|Kt_lo] [U_hi;U_hi] and [Kt_hi|Kt_lo] [U_lo;0].  (One
-        // accumulation chain keeps one MFMA shape: a 16x16x16 that reads the
-        // accumulator of a 16x16x32 issued just before it has been seen to
-        // miss that product.)
-        bf16x8 uu[2], u0[2];
-#pragma unroll
-        for (int vb = 0; vb < 2; ++vb) {
-            uu[vb] = cat8(uh[vb], uh[vb]);
-            u0[vb] = cat8(ul[vb], zb);
-        }
+        // S^T += Kt^T U as [Kt_hi|Kt_lo] [U_hi;U_hi] + [Kt_hi|Kt_lo] [U_lo;U_lo]:
+        // all four hi/lo products in two 16x16x32s.  (One accumulation chain
+        // keeps one MFMA shape: a 16x16x16 that reads the accumulator of a
+        // 16x16x32 issued just before it has been seen to miss that product.)
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-            const bf16x8 t2 = cat8(ld4(&sm.cf_kth[kb * FS], lane), ld4(&sm.cf_ktl[kb * FS], lane));
+            const bf16x8 t2 = *(const bf16x8*)&sm.cf_kt[kb * FS2 + lane * 8];
             const float4 gd = *(const float4*)&sm.gamc[ci & 1][16 * kb + 4 * gq];
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb) {
                 f32x4 s = S[kb][vb];
                 s[0] *= gd.x; s[1] *= gd.y; s[2] *= gd.z; s[3] *= gd.w;
                 s = mma32(t2, uu[vb], s);
-                s = mma32(t2, u0[vb], s);
+                s = mma32(t2, ll[vb], s);
                 S[kb][vb] = s;
             }
         }
