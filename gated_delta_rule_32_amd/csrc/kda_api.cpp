@@ -174,6 +174,7 @@ struct PlanEntry {
     void* dev = nullptr;
     void* host = nullptr;
     hipEvent_t ready = nullptr;
+    bool settled = false;  // the upload behind `ready` was seen complete
     size_t off_task = 0, off_start = 0, off_len = 0, off_tape = 0, off_chunk = 0, off_seg = 0;
     size_t bytes = 0;
 };
@@ -188,16 +189,40 @@ std::vector<int64_t> plan_key(const Prob& p, int dev) {
     return key;
 }
 
+// Under stream capture only a settled cached schedule is usable: the call then
+// enqueues nothing but its kernels.  Outside capture a cached schedule whose
+// upload is still in flight is waited for on the caller's stream.
 kda_status get_plan(const Prob& p, hipStream_t stream, int dev, const PlanEntry** out) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    const bool capturing = cs != hipStreamCaptureStatusNone;
     std::lock_guard<std::mutex> lock(g_mu);
     auto key = plan_key(p, dev);
     auto it = g_plans.find(key);
     if (it != g_plans.end()) {
-        hipError_t e = hipStreamWaitEvent(stream, it->second->ready, 0);
-        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-        *out = it->second.get();
+        PlanEntry* ent = it->second.get();
+        if (!ent->settled && !capturing) {
+            e = hipEventQuery(ent->ready);
+            if (e == hipSuccess)
+                ent->settled = true;
+            else if (e != hipErrorNotReady)
+                return hip_fail(e, "hipEventQuery");
+        }
+        if (!ent->settled) {
+            if (capturing)
+                return fail(KDA_ERR_CAPTURE,
+                            "the schedule for these lengths has not been seen on the device yet; "
+                            "call again outside capture after the first call completed");
+            e = hipStreamWaitEvent(stream, ent->ready, 0);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+        }
+        *out = ent;
         return KDA_OK;
     }
+    if (capturing)
+        return fail(KDA_ERR_CAPTURE,
+                    "no schedule cached for these lengths; make the first call outside capture");
     if (g_plans.size() >= kMaxPlans)
         return fail(KDA_ERR_HIP, "schedule cache full (%zu distinct length sets)", g_plans.size());
     auto ent = std::make_unique<PlanEntry>();
@@ -209,7 +234,7 @@ kda_status get_plan(const Prob& p, hipStream_t stream, int dev, const PlanEntry*
     ent->off_chunk = off; off = align256(off + sizeof(int64_t) * (size_t)(p.N + 1));
     ent->off_seg = off;   off = align256(off + sizeof(int32_t) * 2 * (size_t)p.total_segs);
     ent->bytes = off;
-    hipError_t e = hipHostMalloc(&ent->host, ent->bytes, hipHostMallocDefault);
+    e = hipHostMalloc(&ent->host, ent->bytes, hipHostMallocDefault);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(schedule)");
     char* h = (char*)ent->host;
     std::vector<int32_t> order = lpt_order(p);
@@ -373,6 +398,7 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_WORKSPACE_SIZE: return "workspace too small";
         case KDA_ERR_ROUTE: return "bad route or checkpoint interval";
         case KDA_ERR_HIP: return "HIP runtime error";
+        case KDA_ERR_CAPTURE: return "schedule not ready for stream capture";
     }
     return "unknown status";
 }

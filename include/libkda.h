@@ -47,6 +47,15 @@
  * the text of the last failure on the calling thread.  Launches are
  * asynchronous on the given stream (a hipStream_t; NULL is the null stream).
  * No entry point synchronises the device.
+ *
+ * Stream capture.  kda_fwd and kda_bwd may be recorded into a HIP graph: under
+ * capture they enqueue kernel launches only (no allocation, copy, memset or
+ * event wait).  That needs the schedule for the call's sequence lengths to be
+ * cached already and known to be on the device: make one call with the same
+ * lengths outside capture, let it complete, then make a second one outside
+ * capture (it observes the upload as finished); otherwise a call under
+ * capture returns KDA_ERR_CAPTURE before touching the stream.  A captured
+ * graph keeps using the cached schedule, which lives until the process ends.
  */
 #ifndef LIBKDA_H
 #define LIBKDA_H
@@ -74,7 +83,10 @@ typedef enum {
     KDA_ERR_CTX_MISMATCH = 9,   /* context not produced by a matching kda_fwd */
     KDA_ERR_WORKSPACE_SIZE = 10,/* workspace smaller than kda_bwd_workspace_bytes() */
     KDA_ERR_ROUTE = 11,         /* unknown route or checkpoint interval */
-    KDA_ERR_HIP = 12            /* a HIP runtime call failed */
+    KDA_ERR_HIP = 12,           /* a HIP runtime call failed */
+    KDA_ERR_CAPTURE = 13        /* called under stream capture before the schedule
+                                   for these lengths was made and had reached the
+                                   device in an earlier call outside capture */
 } kda_status;
 
 typedef enum {

@@ -187,3 +187,12 @@ def test_records_context_sizes_and_rejections():
     p.route = 0
     p.context = 5
     assert _status(kda.kda_fwd_ctx_bytes, p) == 11      # unknown context kind
+
+
+def test_status_strings_cover_every_code():
+    hdr = open(os.path.join(ROOT, "include", "libkda.h")).read()
+    codes = {name: int(val) for name, val in re.findall(r"\b(KDA_(?:OK|ERR_[A-Z_]+))\s*=\s*(\d+)", hdr)}
+    assert codes["KDA_ERR_CAPTURE"] == kda.KDA_ERR_CAPTURE and codes["KDA_ERR_HIP"] == kda.KDA_ERR_HIP
+    texts = {kda.kda_status_string(c) for c in codes.values()}
+    assert len(texts) == len(codes), "two status codes share a description"
+    assert kda.kda_status_string(max(codes.values()) + 1) not in texts

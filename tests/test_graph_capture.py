@@ -1,0 +1,105 @@
+"""kda_fwd and kda_bwd recorded into a HIP graph (torch.cuda.CUDAGraph) and
+replayed: every replay must reproduce the eager results bit for bit (the
+kernels are deterministic), with eager work and synchronisations between the
+replays.  A call under capture whose schedule is not cached yet must fail on
+the host with KDA_ERR_CAPTURE and enqueue nothing.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+P = workloads.Problem
+CASES = {
+    "ragged_tape": (P([1, 15, 16, 17, 33, 100, 300], 2, 4, packed=True), 400, 0),
+    "ragged_records": (P([5, 64, 250], 1, 2, packed=True), 401, 1),
+    "fixed_tape": (P([96] * 2, 2, 2, packed=False), 402, 0),
+}
+
+
+class _Step:
+    """Static buffers for one forward + backward, so that the captured
+    launches keep valid pointers."""
+
+    def __init__(self, inp, context):
+        import gated_delta_rule_32_amd as kda
+        self.kda = kda
+        self.d = d = inp.to("cuda")
+        p = inp.problem
+        self.prob = kda.make_problem(p.B, p.T, p.Hqk, p.Hv, p.N, d.cu_seqlens, inp.cu_seqlens,
+                                     route=1, context=context)
+        self.o = torch.empty_like(d.v)
+        self.fs = torch.empty_like(d.initial_state)
+        self.ctx = torch.empty(kda.kda_fwd_ctx_bytes(self.prob), dtype=torch.uint8, device="cuda")
+        self.ws = torch.empty(kda.kda_bwd_workspace_bytes(self.prob), dtype=torch.uint8, device="cuda")
+        self.grads = [torch.empty_like(x) for x in (d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias,
+                                                    d.initial_state)]
+
+    def outputs(self):
+        return [self.o, self.fs] + self.grads
+
+    def run(self):
+        d, kda = self.d, self.kda
+        h = torch.cuda.current_stream().cuda_stream
+        kda.kda_fwd(self.prob, d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
+                    self.o, self.fs, self.ctx, h)
+        kda.kda_bwd(self.prob, d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
+                    self.ctx, d.do, d.dfinal_state, *self.grads, self.ws, h)
+
+
+def _host(ts):
+    return [t.float().cpu().numpy() for t in ts]
+
+
+@pytest.mark.parametrize("case", list(CASES.keys()))
+def test_captured_step_replays_match_eager(case):
+    problem, seed, context = CASES[case]
+    inp = workloads.make_inputs(problem, seed, with_adjoints=True)
+    print(f"[graph] case={case} lengths={problem.lengths}", flush=True)
+    step = _Step(inp, context)
+    # two eager calls: the first makes and uploads the schedule, the second
+    # (after the device finished) observes the upload as complete
+    step.run()
+    torch.cuda.synchronize()
+    step.run()
+    torch.cuda.synchronize()
+    eager = _host(step.outputs())
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.run()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        # eager work between replays: clobber every output, then replay
+        for t in step.outputs():
+            t.fill_(float("nan") if t.is_floating_point() else 0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _host(step.outputs())
+        for i, (a, b) in enumerate(zip(got, eager)):
+            assert np.array_equal(a, b), f"replay {rep}: output {i} differs from the eager result"
+    # an eager call after the replays still matches as well
+    step.run()
+    torch.cuda.synchronize()
+    for a, b in zip(_host(step.outputs()), eager):
+        assert np.array_equal(a, b)
+
+
+def test_capture_without_cached_schedule_is_refused():
+    import gated_delta_rule_32_amd as kda
+    inp = workloads.make_inputs(P([7, 41, 123], 1, 2, packed=True), 403, with_adjoints=True)
+    step = _Step(inp, kda.CONTEXT_TAPE)
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(kda.KdaValueError) as ei:
+        with torch.cuda.graph(graph):
+            step.run()
+    assert ei.value.status == kda.KDA_ERR_CAPTURE
+    torch.cuda.synchronize()
+    # outside capture the same call works and caches the schedule
+    step.run()
+    torch.cuda.synchronize()
+    assert np.isfinite(step.o.float().cpu().numpy()).all()
