@@ -255,6 +255,8 @@ def main():
                                   "bwd_param_reduce_kernel", "bwd_dqk_reduce_kernel"]}
         if route == 1:
             out["records_context"] = records_context_step(kda, p, d, inp_cpu, args, stream)
+    if p.name == "packed":
+        out["inference"] = inference_steps(kda, p, d, inp_cpu, args, stream)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp_cpu)
     print(json.dumps(out), flush=True)
@@ -299,6 +301,85 @@ def records_context_step(kda, p, d, inp_cpu, args, stream):
     fm, bm = sum(fwd) / len(fwd), sum(bwd) / len(bwd)
     return {"fwd_ms_mean": round(fm, 4), "bwd_ms_mean": round(bm, 4), "step_ms": round(fm + bm, 4),
             "ctx_bytes": ctx_bytes}
+
+
+def inference_steps(kda, p, d, inp_cpu, args, stream):
+    """kda_infer (page "flashinfer.kda.recurrent_kda") on the packed workload's
+    heads, timed with HIP events on the kernels' stream.
+      decode: 256 sequences x 1 token against a BF16 pool of 256 slots in a
+        shuffled order (the page's defaults: log-space gate, beta as a rate);
+      prefill: the packed workload's own tokens with the training settings,
+        starting from its initial states rounded to BF16.
+    Algorithmic bytes per token-head: q, k, v, g, o and beta as in the
+    training forward, plus the BF16 state read and written once per
+    (sequence, head) (2 x 32 KiB)."""
+    import torch
+    import workloads
+    dev = torch.device("cuda")
+    h = stream.cuda_stream
+    res = {}
+    # decode
+    Nd = 256
+    dp = workloads.Problem([1] * Nd, p.Hqk, p.Hv, packed=True, name="decode")
+    di = workloads.make_infer_inputs(dp, 7, 1)          # token tensors; pool drawn below
+    gen = torch.Generator(device=dev).manual_seed(8)
+    pool = (0.1 * torch.randn((Nd, p.Hv, 128, 128), generator=gen, device=dev)).to(torch.bfloat16)
+    idx_cpu = torch.randperm(Nd, generator=torch.Generator().manual_seed(9)).to(torch.int32)
+    idx = idx_cpu.to(dev)
+    t = [x.to(dev) for x in (di.q, di.k, di.v, di.g, di.beta)]
+    o = torch.empty_like(t[2])
+    cu = di.cu_seqlens.to(dev)
+    prob = kda.make_infer_problem(1, Nd, p.Hqk, p.Hv, Nd, Nd, cu, di.cu_seqlens,
+                                  state_indices=idx, state_indices_cpu=idx_cpu)
+
+    prob_c = kda.make_infer_problem(1, Nd, p.Hqk, p.Hv, Nd, Nd, cu, di.cu_seqlens,
+                                    state_indices=idx, state_indices_cpu=idx_cpu, route=1)
+    # the training count holds the FP32 state twice; the pool is BF16
+    bf16_state = lambda prob: algorithmic_fwd_bytes(prob) - prob.N * prob.Hv * 2 * 128 * 128 * 2
+    res["decode"] = _time_infer(lambda: kda.kda_infer(prob, *t, None, None, pool, o, h),
+                                args, stream, Nd * p.Hv, bf16_state(dp))
+    res["decode"]["workload"] = f"{Nd} sequences x 1 token, Hqk={p.Hqk}, Hv={p.Hv}, pool {Nd} slots"
+    res["decode"]["kernel"] = "infer_token_kernel (the automatic route)"
+    res["decode"]["chunk_route_ms_mean"] = _time_infer(
+        lambda: kda.kda_infer(prob_c, *t, None, None, pool, o, h), args, stream, Nd * p.Hv,
+        bf16_state(dp))["ms_mean"]
+    # prefill
+    pool2 = d.initial_state.to(torch.bfloat16)
+    o2 = torch.empty_like(d.v)
+    prob2 = kda.make_infer_problem(p.B, p.T, p.Hqk, p.Hv, p.N, p.N, d.cu_seqlens,
+                                   inp_cpu.cu_seqlens, use_gate_in_kernel=True, lower_bound=-5.0,
+                                   beta_is_logit=True)
+
+    prob2t = kda.make_infer_problem(p.B, p.T, p.Hqk, p.Hv, p.N, p.N, d.cu_seqlens,
+                                    inp_cpu.cu_seqlens, use_gate_in_kernel=True, lower_bound=-5.0,
+                                    beta_is_logit=True, route=2)
+    args2 = (d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, pool2, o2, h)
+    res["prefill"] = _time_infer(lambda: kda.kda_infer(prob2, *args2), args, stream,
+                                 p.token_heads, bf16_state(p))
+    res["prefill"]["workload"] = "the packed workload's tokens, training settings"
+    res["prefill"]["kernel"] = "fwd_chunk_kernel<infer> (the automatic route)"
+    res["prefill"]["token_route_ms_mean"] = _time_infer(
+        lambda: kda.kda_infer(prob2t, *args2), args, stream, p.token_heads, bf16_state(p))["ms_mean"]
+    return res
+
+
+def _time_infer(fn, args, stream, token_heads, nbytes):
+    import torch
+    for _ in range(max(args.warmup, 2)):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms_mean": round(ms, 4), "token_heads_per_s": round(token_heads / (ms * 1e-3), 1),
+            "algorithmic_bytes": int(nbytes), "achieved_GBs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 if __name__ == "__main__":

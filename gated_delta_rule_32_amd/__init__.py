@@ -6,9 +6,11 @@ supplies device memory and the current stream.
 
 Low-level functions carry the C names (kda_fwd, kda_bwd, kda_fwd_ctx_bytes,
 kda_bwd_workspace_bytes, kda_plan_query, kda_status_string, kda_last_error,
-kda_version).  The paired training API mirrors the FlashInfer pages
+kda_version, kda_infer).  The paired training API mirrors the FlashInfer pages
 "flashinfer.kda_training.recurrent_kda_training_forward" and
-"flashinfer.kda_training" (recurrent_kda_training_backward).
+"flashinfer.kda_training" (recurrent_kda_training_backward); recurrent_kda
+covers the decode/prefill subset of page "flashinfer.kda.recurrent_kda"
+(gate, beta and norm options; a BF16 state pool updated in place).
 
 The library must be built first (``python -m gated_delta_rule_32_amd.build_lib``);
 importing this package without it raises.
@@ -53,6 +55,19 @@ class KdaProblem(ctypes.Structure):
     ]
 
 
+class KdaInferProblem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("Hqk", ctypes.c_int32),
+        ("Hv", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+        ("scale", ctypes.c_float), ("use_qk_l2norm", ctypes.c_int32),
+        ("use_gate_in_kernel", ctypes.c_int32), ("lower_bound", ctypes.c_float),
+        ("beta_is_logit", ctypes.c_int32), ("route", ctypes.c_int32),
+        ("pool_slots", ctypes.c_int64),
+        ("state_indices", ctypes.c_void_p), ("state_indices_host", ctypes.c_void_p),
+    ]
+
+
 _P = ctypes.POINTER(KdaProblem)
 _vp = ctypes.c_void_p
 _lib.kda_version.restype = ctypes.c_int
@@ -72,8 +87,11 @@ _lib.kda_bwd.restype = ctypes.c_int
 _lib.kda_bwd.argtypes = ([_P] + [_vp] * 8 + [_vp, ctypes.c_size_t] + [_vp] * 2 + [_vp] * 8
                          + [_vp, ctypes.c_size_t, _vp])
 
+_lib.kda_infer.restype = ctypes.c_int
+_lib.kda_infer.argtypes = [ctypes.POINTER(KdaInferProblem)] + [_vp] * 10
+
 EXPORTED = ("kda_version", "kda_status_string", "kda_last_error", "kda_fwd_ctx_bytes",
-            "kda_bwd_workspace_bytes", "kda_plan_query", "kda_fwd", "kda_bwd")
+            "kda_bwd_workspace_bytes", "kda_plan_query", "kda_fwd", "kda_bwd", "kda_infer")
 
 
 class KdaError(RuntimeError):
@@ -184,6 +202,40 @@ def kda_bwd(p: KdaProblem, q, k, v, g, beta, A_log, dt_bias, initial_state, ctx,
                         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dA_log),
                         _ptr(ddt_bias), _ptr(dinitial_state), _ptr(workspace),
                         workspace.numel() * workspace.element_size(), stream))
+
+
+def make_infer_problem(B: int, T: int, Hqk: int, Hv: int, N: int, pool_slots: int,
+                       cu_seqlens: Optional[torch.Tensor] = None,
+                       cu_seqlens_cpu: Optional[torch.Tensor] = None,
+                       scale: Optional[float] = None, use_qk_l2norm: bool = True,
+                       use_gate_in_kernel: bool = False, lower_bound: Optional[float] = None,
+                       beta_is_logit: bool = False,
+                       state_indices: Optional[torch.Tensor] = None,
+                       state_indices_cpu: Optional[torch.Tensor] = None,
+                       route: int = ROUTE_AUTO) -> KdaInferProblem:
+    p = KdaInferProblem()
+    p.B, p.T, p.Hqk, p.Hv, p.N = int(B), int(T), int(Hqk), int(Hv), int(N)
+    p.cu_seqlens = _ptr(cu_seqlens)
+    p.cu_seqlens_host = _ptr(cu_seqlens_cpu)
+    p.scale = 0.0 if scale is None else float(scale)
+    p.use_qk_l2norm = int(bool(use_qk_l2norm))
+    p.use_gate_in_kernel = int(bool(use_gate_in_kernel))
+    p.lower_bound = 0.0 if lower_bound is None else float(lower_bound)
+    p.beta_is_logit = int(bool(beta_is_logit))
+    p.route = int(route)
+    p.pool_slots = int(pool_slots)
+    p.state_indices = _ptr(state_indices)
+    p.state_indices_host = _ptr(state_indices_cpu)
+    return p
+
+
+def kda_infer(p: KdaInferProblem, q, k, v, g, beta, A_log, dt_bias, state_pool, o,
+              stream: Optional[int] = None) -> None:
+    """C kda_infer on torch tensors."""
+    if stream is None:
+        stream = _stream_handle(q.device)
+    _check(_lib.kda_infer(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                          _ptr(A_log), _ptr(dt_bias), _ptr(state_pool), _ptr(o), stream))
 
 
 # ---------------------------------------------------------------------------
@@ -312,3 +364,66 @@ def recurrent_kda_training_backward(context: RecurrentKDATrainingContext, do, df
     kda_bwd(p, q, k, v, g, beta, A_log, dt_bias, s0, context.ctx, do, dfinal_state, *out,
             workspace, _stream_handle(dev))
     return tuple(out)
+
+
+# ---------------------------------------------------------------------------
+# inference API (decode and prefill on a state pool)
+# ---------------------------------------------------------------------------
+def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initial_state=None,
+                  use_qk_l2norm_in_kernel: bool = True, use_gate_in_kernel: bool = False,
+                  lower_bound=None, cu_seqlens=None, ssm_state_indices=None,
+                  output=None, beta_is_logit: bool = False, *, cu_seqlens_cpu=None,
+                  ssm_state_indices_cpu=None, route: int = ROUTE_AUTO):
+    """Decode / prefill subset of page "flashinfer.kda.recurrent_kda": returns
+    (output, initial_state) with initial_state, a BF16 state pool
+    [P, Hv, 128, 128], updated in place (slot ssm_state_indices[n] for sequence
+    n, or slot n).  Packed calls pass cu_seqlens (int64) with its CPU mirror,
+    and indices with theirs.  route: ROUTE_AUTO, ROUTE_CHUNK (needs every
+    per-token log-decay >= -5) or ROUTE_ROWSPLIT (token-serial, any gate).
+    Speculative decode, state_checkpoints and the softplus gate are not
+    supported."""
+    dev = q.device
+    _require(q.dim() == 4 and v.dim() == 4, "q and v must be [B, T, H, 128]")
+    B, T, Hqk, Dq = q.shape
+    Hv = v.shape[2]
+    _require(Dq == HEAD_DIM and v.shape[3] == HEAD_DIM, "head dimensions must be 128")
+    if cu_seqlens is not None:
+        _require(cu_seqlens_cpu is not None, "packed calls need cu_seqlens_cpu")
+        _require(cu_seqlens.dtype == torch.int64 and cu_seqlens_cpu.dtype == torch.int64,
+                 "cu_seqlens must be int64")
+        _require(cu_seqlens.is_contiguous() and cu_seqlens.device == dev,
+                 "cu_seqlens must be contiguous on the device of q")
+        _require(cu_seqlens_cpu.device.type == "cpu" and cu_seqlens_cpu.is_contiguous(),
+                 "cu_seqlens_cpu must be a contiguous CPU tensor")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    _require(initial_state is not None, "initial_state (the BF16 state pool) is required")
+    _require(initial_state.dim() == 4 and tuple(initial_state.shape[1:]) == (Hv, 128, 128),
+             "initial_state must be [P, Hv, 128, 128]")
+    P = initial_state.shape[0]
+    bf = torch.bfloat16
+    _check_tensor("initial_state", initial_state, bf, (P, Hv, 128, 128), dev)
+    _check_tensor("q", q, bf, (B, T, Hqk, 128), dev)
+    _check_tensor("k", k, bf, (B, T, Hqk, 128), dev)
+    _check_tensor("v", v, bf, (B, T, Hv, 128), dev)
+    _check_tensor("g", g, bf, (B, T, Hv, 128), dev)
+    _check_tensor("beta", beta, bf, (B, T, Hv), dev)
+    if A_log is not None:
+        _check_tensor("A_log", A_log, torch.float32, (Hv,), dev)
+    if dt_bias is not None:
+        dt_bias = dt_bias.reshape(Hv, 128) if dt_bias.dim() == 1 else dt_bias
+        _check_tensor("dt_bias", dt_bias, torch.float32, (Hv, 128), dev)
+    if ssm_state_indices is not None:
+        _require(ssm_state_indices_cpu is not None, "ssm_state_indices needs its CPU mirror")
+        _check_tensor("ssm_state_indices", ssm_state_indices, torch.int32, (N,), dev)
+        _require(ssm_state_indices_cpu.dtype == torch.int32 and
+                 ssm_state_indices_cpu.device.type == "cpu" and ssm_state_indices_cpu.is_contiguous(),
+                 "ssm_state_indices_cpu must be a contiguous int32 CPU tensor")
+    o = output if output is not None else torch.empty((B, T, Hv, 128), dtype=bf, device=dev)
+    _check_tensor("output", o, bf, (B, T, Hv, 128), dev)
+    p = make_infer_problem(B, T, Hqk, Hv, N, P, cu_seqlens, cu_seqlens_cpu, scale,
+                           use_qk_l2norm_in_kernel, use_gate_in_kernel, lower_bound, beta_is_logit,
+                           ssm_state_indices, ssm_state_indices_cpu, route)
+    kda_infer(p, q, k, v, g, beta, A_log, dt_bias, initial_state, o)
+    return o, initial_state

@@ -33,6 +33,7 @@ SOURCES = [
     "kda_fwd_rowsplit.hip",
     "kda_fwd_chunk.hip",
     "kda_bwd.hip",
+    "kda_infer.hip",
 ]
 
 FLAGS = [

@@ -614,4 +614,99 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
     return KDA_OK;
 }
 
+kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, const void* v,
+                     const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                     void* state_pool, void* o, void* stream_) {
+    if (ip == nullptr) return fail(KDA_ERR_NULL_ARG, "problem is NULL");
+    // shape, grouping and sequence checks are the training forward's
+    kda_problem tp{};
+    tp.B = ip->B; tp.T = ip->T; tp.Hqk = ip->Hqk; tp.Hv = ip->Hv; tp.N = ip->N;
+    tp.cu_seqlens = ip->cu_seqlens;
+    tp.cu_seqlens_host = ip->cu_seqlens_host;
+    tp.scale = 0.0f;
+    tp.lower_bound = -5.0f;
+    tp.route = KDA_ROUTE_ROWSPLIT;
+    tp.checkpoint_every = 0;
+    tp.context = KDA_CONTEXT_TAPE;
+    Prob p;
+    kda_status s = validate(&tp, p);
+    if (s != KDA_OK) return s;
+    float scale = ip->scale == 0.0f ? 1.0f / std::sqrt(128.0f) : ip->scale;
+    if (!(scale > 0.0f) || !std::isfinite(scale))
+        return fail(KDA_ERR_SCALE, "scale must be 0 or finite and positive (got %g)", (double)ip->scale);
+    for (int32_t f : {ip->use_qk_l2norm, ip->use_gate_in_kernel, ip->beta_is_logit})
+        if (f != 0 && f != 1) return fail(KDA_ERR_SHAPE, "option flags must be 0 or 1 (got %d)", f);
+    if (ip->route < 0 || ip->route > 2) return fail(KDA_ERR_ROUTE, "unknown route %d", ip->route);
+    const bool bounded_gate = ip->use_gate_in_kernel && ip->lower_bound >= -5.0f;
+    if (ip->route == KDA_ROUTE_CHUNK && ip->use_gate_in_kernel && !bounded_gate)
+        return fail(KDA_ERR_ROUTE, "the chunked route needs lower_bound >= -5 (got %g)",
+                    (double)ip->lower_bound);
+    if (ip->use_gate_in_kernel) {
+        if (!(ip->lower_bound < 0.0f) || !std::isfinite(ip->lower_bound))
+            return fail(KDA_ERR_LOWER_BOUND,
+                        "the in-kernel gate needs a finite negative lower_bound (got %g); the "
+                        "softplus form is not implemented", (double)ip->lower_bound);
+        if (A_log == nullptr) return fail(KDA_ERR_NULL_ARG, "the in-kernel gate needs A_log");
+    }
+    if (!q || !k || !v || !g || !beta || !state_pool || !o)
+        return fail(KDA_ERR_NULL_ARG, "a tensor argument of kda_infer is NULL");
+    if (ip->pool_slots < 1 || ip->pool_slots > ((int64_t)1 << 40) / ((int64_t)p.Hv * kStateElems))
+        return fail(KDA_ERR_SHAPE, "pool_slots out of range (%lld)", (long long)ip->pool_slots);
+    if ((ip->state_indices == nullptr) != (ip->state_indices_host == nullptr))
+        return fail(KDA_ERR_NULL_ARG, "state_indices and state_indices_host go together");
+    if (ip->state_indices_host != nullptr) {
+        std::vector<int32_t> sorted(ip->state_indices_host, ip->state_indices_host + p.N);
+        for (int n = 0; n < p.N; ++n) {
+            const int32_t slot = sorted[n];
+            if (slot < 0 || slot >= ip->pool_slots)
+                return fail(KDA_ERR_SHAPE, "state_indices[%d] = %d is outside the pool", n, slot);
+        }
+        std::sort(sorted.begin(), sorted.end());
+        for (int n = 1; n < p.N; ++n)
+            if (sorted[n] == sorted[n - 1])
+                return fail(KDA_ERR_SHAPE, "pool slot %d is named twice", sorted[n]);
+    } else if (ip->pool_slots < p.N) {
+        return fail(KDA_ERR_SHAPE, "without state_indices the pool needs N=%d slots (has %lld)", p.N,
+                    (long long)ip->pool_slots);
+    }
+    const size_t tq = (size_t)p.tokens * p.Hqk * D * 2;
+    const size_t tv = (size_t)p.tokens * p.Hv * D * 2;
+    std::vector<Span> ins = {{q, tq, "q"}, {k, tq, "k"}, {v, tv, "v"}, {g, tv, "g"},
+                             {beta, (size_t)p.tokens * p.Hv * 2, "beta"},
+                             {A_log, A_log ? (size_t)p.Hv * 4 : 0, "A_log"},
+                             {dt_bias, dt_bias ? (size_t)p.Hv * D * 4 : 0, "dt_bias"},
+                             {ip->cu_seqlens, ip->cu_seqlens ? (size_t)(p.N + 1) * 8 : 0, "cu_seqlens"},
+                             {ip->state_indices, ip->state_indices ? (size_t)p.N * 4 : 0,
+                              "state_indices"}};
+    const size_t pool_bytes = (size_t)ip->pool_slots * p.Hv * kStateElems * 2;
+    std::vector<Span> outs = {{o, tv, "o"}, {state_pool, pool_bytes, "state_pool"}};
+    s = check_overlap(outs, ins);
+    if (s != KDA_OK) return s;
+
+    hipStream_t stream = (hipStream_t)stream_;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    const PlanEntry* plan = nullptr;
+    s = get_plan(p, stream, dev, &plan);
+    if (s != KDA_OK) return s;
+    kda::FwdArgs a = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, nullptr);
+    const int64_t longest = *std::max_element(p.len.begin(), p.len.end());
+    const int route = ip->route != KDA_ROUTE_AUTO ? ip->route
+                      : (bounded_gate && longest > 1) ? KDA_ROUTE_CHUNK : KDA_ROUTE_ROWSPLIT;
+    a.o = o;
+    a.scale = scale;
+    a.infer = 1;
+    a.use_qk_l2norm = ip->use_qk_l2norm;
+    a.use_gate_in_kernel = ip->use_gate_in_kernel;
+    a.beta_is_logit = ip->beta_is_logit;
+    a.lower_bound = ip->lower_bound;
+    a.pool = (kda::bf16_t*)state_pool;
+    a.pool_index = ip->state_indices;
+    a.pool_slots = ip->pool_slots;
+    e = route == KDA_ROUTE_CHUNK ? kda::launch_fwd_chunk(a, stream) : kda::launch_infer_token(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "inference launch");
+    return KDA_OK;
+}
+
 }  // extern "C"

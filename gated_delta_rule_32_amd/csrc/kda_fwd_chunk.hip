@@ -122,14 +122,21 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], 
 // output, and stores for every chunk the records the adjoint reads
 // (chunk-start state, U, T, Akk, Aqk).  kMode = kFwdRecords: the training
 // forward that stores those records for every chunk instead of the tape, so
-// that the backward reruns nothing.
-constexpr int kFwdTape = 0, kFwdRebuild = 1, kFwdRecords = 2;
+// that the backward reruns nothing.  kMode = kFwdInfer: the inference forward
+// of page "flashinfer.kda.recurrent_kda" (no tape): the state comes from a
+// BF16 pool slot and goes back to it, and the prologue follows the call's
+// options (L2 norm on or off, in-kernel gate with its lower bound or a
+// log-space gate as given, beta as a logit or as given).  The chunk form
+// needs every per-token log-decay at or above -5 (so that the factors
+// exp(+-gc) stay in range); the host routes other calls elsewhere.
+constexpr int kFwdTape = 0, kFwdRebuild = 1, kFwdRecords = 2, kFwdInfer = 3;
 
 template <int kMode>
 __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     constexpr bool kRebuild = kMode == kFwdRebuild;  // one segment, no output
     constexpr bool kOut = kMode != kFwdRebuild;      // o and the final state
-    constexpr bool kRec = kMode != kFwdTape;         // per-chunk records
+    constexpr bool kRec = kMode == kFwdRebuild || kMode == kFwdRecords;  // per-chunk records
+    constexpr bool kInfer = kMode == kFwdInfer;      // BF16 pool state, prologue options
     __shared__ FwdLds sm;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -163,6 +170,14 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         if (seg > 0) src = a.tape + ((tape_base + seg - 1) * a.Hv + h) * (int64_t)D * D;
     }
     if constexpr (kRec) rec0 = a.plan.chunk_off[n];
+    // inference: the pool slot of sequence n (checked on the host; a slot
+    // out of range ends the workgroup before any access or barrier)
+    bf16* pslab = nullptr;
+    if constexpr (kInfer) {
+        const int64_t slot = a.pool_index != nullptr ? a.pool_index[n] : n;
+        if (slot < 0 || slot >= a.pool_slots) return;
+        pslab = (bf16*)a.pool + (slot * a.Hv + h) * (int64_t)D * D;
+    }
 
     // state: S^T frags for kb = 0..7 and vb = 2*wave + {0, 1}
     f32x4 S[8][2];
@@ -173,16 +188,25 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int vcol = 16 * (2 * wave + j) + cl;
-                const float4 x = *(const float4*)(src + (int64_t)vcol * D + 16 * kb + 4 * gq);
-                S[kb][j] = f32x4{x.x, x.y, x.z, x.w};
+                if constexpr (kInfer) {
+                    S[kb][j] = from_bf4(*(const bf16x4*)(pslab + vcol * D + 16 * kb + 4 * gq));
+                } else {
+                    const float4 x = *(const float4*)(src + (int64_t)vcol * D + 16 * kb + 4 * gq);
+                    S[kb][j] = f32x4{x.x, x.y, x.z, x.w};
+                }
             }
     }
 
-    const float eA = __expf(a.A_log[h]);
+    // prologue options (inference only; the training modes fix them)
+    const bool gate_in = !kInfer || a.use_gate_in_kernel != 0;
+    const bool l2norm = !kInfer || a.use_qk_l2norm != 0;
+    const bool beta_logit = !kInfer || a.beta_is_logit != 0;
+    const float lb2 = (kInfer ? a.lower_bound : -5.0f) * LOG2E;  // log2-domain lower bound
+    const float eA = gate_in ? __expf(a.A_log[h]) : 0.f;
     // z*log2(e) = g*(eA log2e) + dt*(eA log2e); the log2-domain decay is
     // -5 log2(e) sigmoid(z)
     const float zs = eA * LOG2E;
-    if (tid < D) sm.dtz[tid] = a.dt_bias[h * D + tid] * zs;
+    if (tid < D) sm.dtz[tid] = (gate_in && a.dt_bias != nullptr) ? a.dt_bias[h * D + tid] * zs : 0.f;
 
     SeqPtrs sp;
     sp.q = (const bf16*)a.q + (tok0 * a.Hqk + hq) * D;
@@ -227,20 +251,24 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         sq = row16_sum(sq);
         sk = row16_sum(sk);
         // the output scale rides on the query norm: O = (s Qg) S0^T + (s Aqk) U
-        rq = (a.scale * vm) * fast_rsqrt(sq + 1e-6f);
-        rk = vm * fast_rsqrt(sk + 1e-6f);
+        rq = (a.scale * vm) * (l2norm ? fast_rsqrt(sq + 1e-6f) : 1.0f);
+        rk = vm * (l2norm ? fast_rsqrt(sk + 1e-6f) : 1.0f);
         float lv[8], dz[8];
         *(float4*)&dz[0] = *(const float4*)&sm.dtz[c8];
         *(float4*)&dz[4] = *(const float4*)&sm.dtz[c8 + 4];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float e = __builtin_amdgcn_exp2f(-((float)cur.g[i] * zs + dz[i]));
-            lv[i] = ((-5.0f * LOG2E) * vm) * __builtin_amdgcn_rcpf(1.0f + e);
+            if (kInfer && !gate_in) {  // a log-space decay as given
+                lv[i] = (LOG2E * vm) * (float)cur.g[i];
+            } else {
+                const float e = __builtin_amdgcn_exp2f(-((float)cur.g[i] * zs + dz[i]));
+                lv[i] = (lb2 * vm) * __builtin_amdgcn_rcpf(1.0f + e);
+            }
         }
         *(float4*)&sm.lam[r][c8] = make_float4(lv[0], lv[1], lv[2], lv[3]);
         *(float4*)&sm.lam[r][c8 + 4] = make_float4(lv[4], lv[5], lv[6], lv[7]);
         // the row's 16 lanes store the same value (no branch)
-        sm.beta[ci & 1][r] = vm * sigmoidf_((float)cur.b);
+        sm.beta[ci & 1][r] = vm * (beta_logit ? sigmoidf_((float)cur.b) : (float)cur.b);
     };
     // ---- B: in-place prefix sums of chunk ci's decays over its tokens, and
     // exp(gC).  Every wave takes 32 channels: lanes 0-31 sum rows 0-7, lanes
@@ -554,13 +582,26 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     const int cfull = min(ce, nfull);
     for (int ci = cb; ci < cfull; ++ci) chunk(ci, std::false_type{});
     if (nfull < ce) chunk(nfull, std::true_type{});
-    if (kOut && a.s_final != nullptr)
+    if constexpr (kInfer) {
+        const int lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int vcol = 16 * (2 * wave + j) + cl;
+                *(bf16x4*)(pslab + vcol * D + 16 * kb + 4 * gq) = to_bf4(S[kb][j]);
+            }
+    } else if (kOut && a.s_final != nullptr) {
         store_state(a.s_final + slab, S, wave, (tid & 63) >> 4, tid & 15);
+    }
 }
 
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s) {
     if (a.num_tasks == 0) return hipSuccess;
-    if (a.rec_s0 != nullptr)
+    if (a.infer)
+        hipLaunchKernelGGL(fwd_chunk_kernel<kFwdInfer>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0,
+                           s, a);
+    else if (a.rec_s0 != nullptr)
         hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRecords>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0,
                            s, a);
     else

@@ -47,6 +47,16 @@ struct FwdArgs {
     // state rebuild mode: process only the tokens of tape segment `seg`
     // (0 = from the initial state); -1 = whole sequence
     int seg_mode;
+    // Inference (infer_token_kernel): prologue options and the BF16 state
+    // pool [pool_slots][Hv][128][128] read and written in place at slot
+    // pool_index[n] (slot n when pool_index is null); s0, s_final and tape
+    // are unused.
+    int infer;
+    int use_qk_l2norm, use_gate_in_kernel, beta_is_logit;
+    float lower_bound;
+    bf16_t* pool;
+    const int32_t* pool_index;
+    int64_t pool_slots;
 };
 
 struct BwdArgs {
@@ -61,6 +71,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd_rowsplit(const FwdArgs& a, hipStream_t s);
+hipError_t launch_infer_token(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s);
 hipError_t launch_state_rebuild(const FwdArgs& a, int64_t num_items, hipStream_t s);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);

@@ -183,6 +183,63 @@ kda_status kda_bwd(const kda_problem* p,
                    float* dA_log, float* ddt_bias, float* dinitial_state,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Inference forward (page "flashinfer.kda.recurrent_kda"): decode (one
+ * token per sequence) and prefill on a BF16 state pool updated in place.
+ * The shape fields mean what they mean in kda_problem.  The options follow
+ * the page's parameters:
+ *   use_qk_l2norm       nonzero: L2-normalise q and k (epsilon 1e-6);
+ *                       zero: use them as given;
+ *   use_gate_in_kernel  nonzero: per-channel decay
+ *                       exp(lower_bound * sigmoid(exp(A_log) * (g + dt_bias)))
+ *                       (A_log required, dt_bias NULL counts as zero);
+ *                       zero: g is the log-space decay, applied as exp(g)
+ *                       (A_log and dt_bias unused, may be NULL);
+ *   lower_bound         with use_gate_in_kernel a finite negative value; 0
+ *                       (unset) is refused, as the page's softplus form is
+ *                       not implemented;
+ *   beta_is_logit       nonzero: beta = sigmoid(input); zero: used as given.
+ * scale: 0 selects 1/sqrt(128), otherwise any finite positive value.
+ * The state pool is BF16 [pool_slots][Hv][128][128], value-first ([v][k]).
+ * Sequence n starts from slot state_indices[n] (slot n when state_indices is
+ * NULL, which needs pool_slots >= N) and its final state is rounded to BF16
+ * and written back to that slot; other slots are not touched.  The indices
+ * must be distinct and in [0, pool_slots): they are checked on the host
+ * mirror state_indices_host (given iff state_indices is).
+ * Layout: q, k [B][T][Hqk][128], v, g [B][T][Hv][128], beta [B][T][Hv] BF16;
+ * A_log FP32 [Hv], dt_bias FP32 [Hv][128]; o BF16 [B][T][Hv][128].  The state
+ * runs in FP32 between the pool's load and store.
+ * route: KDA_ROUTE_ROWSPLIT (2) runs the token-serial kernel, exact for any
+ * gate; KDA_ROUTE_CHUNK (1) runs the chunked MFMA kernel, which needs every
+ * per-token log-decay to be >= -5 (always true for the in-kernel gate with
+ * lower_bound >= -5; for a log-space gate the caller vouches for it, as a
+ * smaller one overflows the chunk factors); KDA_ROUTE_AUTO (0) takes the
+ * chunked kernel for the in-kernel gate with lower_bound >= -5 when some
+ * sequence is longer than one token, else the token-serial one.
+ * Asynchronous; capturable under the same condition as kda_fwd. */
+typedef struct {
+    int32_t B;
+    int32_t T;
+    int32_t Hqk;
+    int32_t Hv;
+    int32_t N;
+    const int64_t* cu_seqlens;          /* device INT64 [N+1], or NULL for fixed layout */
+    const int64_t* cu_seqlens_host;     /* host INT64 [N+1] mirror, NULL iff cu_seqlens is NULL */
+    float scale;
+    int32_t use_qk_l2norm;
+    int32_t use_gate_in_kernel;
+    float lower_bound;
+    int32_t beta_is_logit;
+    int32_t route;
+    int64_t pool_slots;
+    const int32_t* state_indices;       /* device INT32 [N], or NULL */
+    const int32_t* state_indices_host;  /* host INT32 [N] mirror, NULL iff state_indices is NULL */
+} kda_infer_problem;
+
+kda_status kda_infer(const kda_infer_problem* p,
+                     const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* A_log, const float* dt_bias,
+                     void* state_pool, void* o, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

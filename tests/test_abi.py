@@ -196,3 +196,53 @@ def test_status_strings_cover_every_code():
     texts = {kda.kda_status_string(c) for c in codes.values()}
     assert len(texts) == len(codes), "two status codes share a description"
     assert kda.kda_status_string(max(codes.values()) + 1) not in texts
+
+
+def test_infer_rejections_before_device_work():
+    """kda_infer checks its options, pool indices and buffers on the host
+    (page "flashinfer.kda.recurrent_kda", parameters)."""
+    lib = kda._lib
+    nb = 16 * 128 * 2
+    base = 0x10000000
+    q, k, v, g, beta = (base + i * nb for i in range(5))
+    A, dtb = base + 6 * nb, base + 7 * nb
+    pool = base + 64 * nb
+    o = base + 2000 * nb
+
+    def call(p, A_ptr=A, o_ptr=o, pool_ptr=pool):
+        return lib.kda_infer(ctypes.byref(p), q, k, v, g, beta, A_ptr, dtb, pool_ptr, o_ptr, None)
+
+    def prob(**kw):
+        base_kw = dict(B=1, T=16, Hqk=1, Hv=1, N=1, pool_slots=1)
+        base_kw.update(kw)
+        return kda.make_infer_problem(**base_kw)
+
+    # in-kernel gate needs a lower bound (softplus form not implemented) and A_log
+    assert call(prob(use_gate_in_kernel=True)) == 6
+    assert call(prob(use_gate_in_kernel=True, lower_bound=2.0)) == 6
+    assert call(prob(use_gate_in_kernel=True, lower_bound=-3.0), A_ptr=None) == 1
+    # routes: unknown, or the chunked one with a gate it cannot bound
+    assert call(prob(route=3)) == 11
+    assert call(prob(use_gate_in_kernel=True, lower_bound=-6.0, route=1)) == 11
+    # scale must be positive
+    assert call(prob(scale=-1.0)) == 5
+    # option flags are 0 or 1
+    p = prob()
+    p.beta_is_logit = 2
+    assert call(p) == 2
+    # pool too small for slot n without indices
+    assert call(kda.make_infer_problem(B=2, T=16, Hqk=1, Hv=1, N=2, pool_slots=1)) == 2
+    # indices: out of range, repeated, or without their host mirror
+    cu = torch.tensor([0, 5, 16], dtype=torch.int64)
+    for bad in ([0, 3], [1, 1], [-1, 0]):
+        idx = torch.tensor(bad, dtype=torch.int32)
+        p = kda.make_infer_problem(1, 16, 1, 1, 2, 3, cu, cu, state_indices=idx,
+                                   state_indices_cpu=idx)
+        assert call(p) == 2, bad
+    idx = torch.tensor([2, 0], dtype=torch.int32)
+    p = kda.make_infer_problem(1, 16, 1, 1, 2, 3, cu, cu, state_indices=idx)
+    assert call(p) == 1
+    # output overlapping the pool or an input
+    assert call(prob(), o_ptr=pool + 64) == 7
+    assert call(prob(), o_ptr=v) == 7
+    assert call(prob(), pool_ptr=q + 2) == 7

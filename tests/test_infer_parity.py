@@ -1,0 +1,122 @@
+"""GPU parity of the inference forward kda_infer (page
+"flashinfer.kda.recurrent_kda": decode and prefill with the gate, beta and
+norm options, on a BF16 state pool updated in place) against the FP64
+inference oracle, through the C ABI.
+
+Bar: the output and the updated pool slots (both BF16) within the pages'
+validation bar |x - ref| <= 1e-2 + 1e-2 |ref| plus the Frobenius bar of
+parity_util; pool slots no sequence names must come back bit for bit.  Every
+case runs on the token-serial kernel and, where its per-token log-decays stay
+at or above -5, on the chunked kernel as well.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import kda_infer_oracle as kio
+from tests import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+P = workloads.Problem
+# name: (problem, seed, pool_slots, options, generator options)
+CASES = {
+    # one token per sequence against a pool with spare slots, the page's defaults
+    "decode_defaults": (P([1] * 48, 2, 4, packed=True), 500, 64,
+                        dict(), dict()),
+    # ragged prefill with the training settings (in-kernel gate, beta logits)
+    "prefill_training_gate": (P([1, 15, 16, 17, 33, 100], 2, 4, packed=True), 501, 8,
+                              dict(use_gate_in_kernel=True, lower_bound=-5.0, beta_is_logit=True),
+                              dict(log_gate_min=None, beta_logits=True)),
+    # another lower bound, and no dt_bias
+    "prefill_lb3_no_dt_bias": (P([40, 7, 64], 1, 2, packed=True), 502, 3,
+                               dict(use_gate_in_kernel=True, lower_bound=-3.0, no_dt_bias=True),
+                               dict(log_gate_min=None)),
+    # q, k used as given (near-unit draws)
+    "prefill_no_norm": (P([30, 50], 2, 2, packed=True), 503, 2,
+                        dict(use_qk_l2norm=False), dict(qk_std=128 ** -0.5)),
+    # log-space gates down to -20 per token: no range limit on this route
+    "prefill_strong_log_gate": (P([37, 80], 1, 1, packed=True), 504, 5,
+                                dict(), dict(log_gate_min=-20.0)),
+    # fixed layout, pool slot n for sequence n
+    "fixed_identity_slots": (P([40] * 3, 1, 2, packed=False), 505, 3,
+                             dict(identity_slots=True), dict()),
+}
+
+
+def _binding_opts(opts):
+    # the page's parameter name for the norm option
+    out = dict(opts)
+    if "use_qk_l2norm" in out:
+        out["use_qk_l2norm_in_kernel"] = out.pop("use_qk_l2norm")
+    return out
+
+
+# cases whose log-decays can fall below -5 per token: token-serial route only
+TOKEN_ONLY = {"prefill_strong_log_gate"}
+ROUTES = {"chunk": 1, "token": 2}
+PARAMS = [(c, r) for c in CASES for r in ROUTES if not (r == "chunk" and c in TOKEN_ONLY)]
+
+
+def _run_case(name, route):
+    import gated_delta_rule_32_amd as kda
+    problem, seed, slots, opts, gen_opts = CASES[name]
+    opts = dict(opts)
+    no_dt = opts.pop("no_dt_bias", False)
+    identity = opts.pop("identity_slots", False)
+    inp = workloads.make_infer_inputs(problem, seed, slots, **gen_opts)
+    idx_cpu = None if identity else inp.indices
+    print(f"[infer] case={name} route={route} lengths={problem.lengths[:8]} N={problem.N} "
+          f"slots={slots} options={opts}", flush=True)
+    dev = torch.device("cuda")
+    pool_dev = inp.pool.to(dev)
+    o, pool_out = kda.recurrent_kda(
+        inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev),
+        A_log=inp.A_log.to(dev), dt_bias=None if no_dt else inp.dt_bias.to(dev),
+        initial_state=pool_dev,
+        cu_seqlens=None if inp.cu_seqlens is None else inp.cu_seqlens.to(dev),
+        cu_seqlens_cpu=inp.cu_seqlens,
+        ssm_state_indices=None if idx_cpu is None else idx_cpu.to(dev),
+        ssm_state_indices_cpu=idx_cpu, route=ROUTES[route], **_binding_opts(opts))
+    torch.cuda.synchronize()
+    assert pool_out.data_ptr() == pool_dev.data_ptr()
+    o_ref, pool_ref = kio.infer_forward(
+        inp.q, inp.k, inp.v, inp.g, inp.beta, inp.A_log, None if no_dt else inp.dt_bias,
+        inp.pool, problem.lengths, problem.packed,
+        indices=None if idx_cpu is None else idx_cpu.tolist(), **opts)
+    return problem, inp, idx_cpu, o.float().cpu().numpy(), pool_dev.float().cpu().numpy(), \
+        o_ref, pool_ref
+
+
+@pytest.mark.parametrize("case,route", PARAMS)
+def test_infer_matches_oracle(case, route):
+    problem, inp, idx_cpu, o, pool, o_ref, pool_ref = _run_case(case, route)
+    named = list(range(problem.N)) if idx_cpu is None else idx_cpu.tolist()
+    rest = [s for s in range(pool.shape[0]) if s not in set(named)]
+    pu.report_and_check([("o", o, o_ref), ("state_pool", pool[named], pool_ref[named])])
+    before = inp.pool.float().numpy()
+    for s in rest:
+        assert np.array_equal(pool[s], before[s]), f"pool slot {s} changed but no sequence names it"
+
+
+@pytest.mark.parametrize("route", list(ROUTES.keys()))
+def test_infer_training_settings_match_training_forward(route):
+    """With the training settings and the pool holding the BF16-rounded
+    initial states, the output matches the training forward's (both within
+    the bar of the FP64 oracle, checked above); here the two GPU paths are
+    compared directly on the same draws."""
+    import gated_delta_rule_32_amd as kda
+    problem = P([9, 40, 23], 2, 2, packed=True)
+    inp = workloads.make_inputs(problem, 506, with_adjoints=False)
+    s0_bf = inp.initial_state.to(torch.bfloat16)
+    inp.initial_state = s0_bf.float()
+    o_t, fs_t, _ctx, d = pu.run_forward(inp, save_context=False)
+    pool = s0_bf.to("cuda")
+    o_i, _ = kda.recurrent_kda(d.q, d.k, d.v, d.g, d.beta, A_log=d.A_log, dt_bias=d.dt_bias,
+                               initial_state=pool, use_gate_in_kernel=True, lower_bound=-5.0,
+                               beta_is_logit=True, cu_seqlens=d.cu_seqlens,
+                               cu_seqlens_cpu=inp.cu_seqlens, route=ROUTES[route])
+    torch.cuda.synchronize()
+    pu.report_and_check([("o", o_i.float().cpu().numpy(), o_t.float().cpu().numpy()),
+                         ("final_state", pool.float().cpu().numpy(), fs_t.cpu().numpy())])

@@ -175,3 +175,51 @@ def sequence_slices(problem: Problem):
         for n, L in enumerate(problem.lengths):
             out.append((n, n, 0, int(L)))
     return out
+
+
+@dataclass
+class InferInputs:
+    """One inference call (page "flashinfer.kda.recurrent_kda"): token tensors
+    as in the training contract, a BF16 state pool [P, Hv, 128, 128] and the
+    pool slot of every sequence."""
+    problem: Problem
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    A_log: torch.Tensor
+    dt_bias: torch.Tensor
+    pool: torch.Tensor
+    indices: torch.Tensor
+    cu_seqlens: Optional[torch.Tensor]
+
+
+def make_infer_inputs(problem: Problem, seed: int, pool_slots: int, log_gate_min: float = -5.0,
+                      beta_logits: bool = False, qk_std: float = 1.0) -> InferInputs:
+    """Draw order (CPU generator seeded with `seed`): q, k (qk_std * randn,
+    BF16), v (randn, BF16), g, beta, A_log = 2*rand, dt_bias = 0.1*randn,
+    pool = 0.1*randn (BF16), indices = the first N of a permutation of the
+    pool's slots.  g is a raw gate input (randn) when log_gate_min is None,
+    else a log-space decay uniform in (log_gate_min, 0); beta is a logit
+    (randn) or a rate uniform in (0, 1).  qk_std near 1/sqrt(128) gives
+    near-unit keys for calls that skip the L2 norm."""
+    gen = torch.Generator().manual_seed(seed)
+    B, T, Hqk, Hv, N = problem.B, problem.T, problem.Hqk, problem.Hv, problem.N
+    q = (qk_std * torch.randn((B, T, Hqk, DIM), generator=gen)).to(torch.bfloat16)
+    k = (qk_std * torch.randn((B, T, Hqk, DIM), generator=gen)).to(torch.bfloat16)
+    v = _randn_bf16(gen, (B, T, Hv, DIM))
+    if log_gate_min is None:
+        g = _randn_bf16(gen, (B, T, Hv, DIM))
+    else:
+        g = (log_gate_min * torch.rand((B, T, Hv, DIM), generator=gen)).to(torch.bfloat16)
+    if beta_logits:
+        beta = _randn_bf16(gen, (B, T, Hv))
+    else:
+        beta = torch.rand((B, T, Hv), generator=gen).to(torch.bfloat16)
+    A_log = 2.0 * torch.rand((Hv,), generator=gen, dtype=torch.float32)
+    dt_bias = 0.1 * torch.randn((Hv, DIM), generator=gen, dtype=torch.float32)
+    pool = (0.1 * torch.randn((pool_slots, Hv, DIM, DIM), generator=gen)).to(torch.bfloat16)
+    indices = torch.randperm(pool_slots, generator=gen)[:N].to(torch.int32)
+    return InferInputs(problem, q, k, v, g, beta, A_log, dt_bias, pool, indices,
+                       problem.cu_seqlens())
