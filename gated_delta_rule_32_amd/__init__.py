@@ -65,6 +65,9 @@ class KdaInferProblem(ctypes.Structure):
         ("beta_is_logit", ctypes.c_int32), ("route", ctypes.c_int32),
         ("pool_slots", ctypes.c_int64),
         ("state_indices", ctypes.c_void_p), ("state_indices_host", ctypes.c_void_p),
+        ("checkpoint_every", ctypes.c_int32), ("state_checkpoints", ctypes.c_void_p),
+        ("checkpoint_rows", ctypes.c_int64), ("checkpoint_cu_starts", ctypes.c_void_p),
+        ("checkpoint_cu_starts_host", ctypes.c_void_p),
     ]
 
 
@@ -212,7 +215,10 @@ def make_infer_problem(B: int, T: int, Hqk: int, Hv: int, N: int, pool_slots: in
                        beta_is_logit: bool = False,
                        state_indices: Optional[torch.Tensor] = None,
                        state_indices_cpu: Optional[torch.Tensor] = None,
-                       route: int = ROUTE_AUTO) -> KdaInferProblem:
+                       route: int = ROUTE_AUTO, checkpoint_every: int = 0,
+                       state_checkpoints: Optional[torch.Tensor] = None,
+                       checkpoint_cu_starts: Optional[torch.Tensor] = None,
+                       checkpoint_cu_starts_cpu: Optional[torch.Tensor] = None) -> KdaInferProblem:
     p = KdaInferProblem()
     p.B, p.T, p.Hqk, p.Hv, p.N = int(B), int(T), int(Hqk), int(Hv), int(N)
     p.cu_seqlens = _ptr(cu_seqlens)
@@ -226,6 +232,11 @@ def make_infer_problem(B: int, T: int, Hqk: int, Hv: int, N: int, pool_slots: in
     p.pool_slots = int(pool_slots)
     p.state_indices = _ptr(state_indices)
     p.state_indices_host = _ptr(state_indices_cpu)
+    p.checkpoint_every = int(checkpoint_every)
+    p.state_checkpoints = _ptr(state_checkpoints)
+    p.checkpoint_rows = 0 if state_checkpoints is None else int(state_checkpoints.shape[0])
+    p.checkpoint_cu_starts = _ptr(checkpoint_cu_starts)
+    p.checkpoint_cu_starts_host = _ptr(checkpoint_cu_starts_cpu)
     return p
 
 
@@ -372,16 +383,21 @@ def recurrent_kda_training_backward(context: RecurrentKDATrainingContext, do, df
 def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initial_state=None,
                   use_qk_l2norm_in_kernel: bool = True, use_gate_in_kernel: bool = False,
                   lower_bound=None, cu_seqlens=None, ssm_state_indices=None,
-                  output=None, beta_is_logit: bool = False, *, cu_seqlens_cpu=None,
-                  ssm_state_indices_cpu=None, route: int = ROUTE_AUTO):
+                  output=None, beta_is_logit: bool = False, state_checkpoints=None,
+                  checkpoint_cu_starts=None, checkpoint_every_n_tokens: int = 0, *,
+                  cu_seqlens_cpu=None, ssm_state_indices_cpu=None, checkpoint_cu_starts_cpu=None,
+                  route: int = ROUTE_AUTO):
     """Decode / prefill subset of page "flashinfer.kda.recurrent_kda": returns
     (output, initial_state) with initial_state, a BF16 state pool
     [P, Hv, 128, 128], updated in place (slot ssm_state_indices[n] for sequence
     n, or slot n).  Packed calls pass cu_seqlens (int64) with its CPU mirror,
     and indices with theirs.  route: ROUTE_AUTO, ROUTE_CHUNK (needs every
     per-token log-decay >= -5) or ROUTE_ROWSPLIT (token-serial, any gate).
-    Speculative decode, state_checkpoints and the softplus gate are not
-    supported."""
+    With checkpoint_every_n_tokens = E > 0, state_checkpoints (BF16
+    [C, Hv, 128, 128]) receives, from row checkpoint_cu_starts[n] on, the
+    states of sequence n before tokens 0, E, 2E, ... and the call returns
+    (output, initial_state, state_checkpoints).  Speculative decode and the
+    softplus gate are not supported."""
     dev = q.device
     _require(q.dim() == 4 and v.dim() == 4, "q and v must be [B, T, H, 128]")
     B, T, Hqk, Dq = q.shape
@@ -422,8 +438,22 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
                  "ssm_state_indices_cpu must be a contiguous int32 CPU tensor")
     o = output if output is not None else torch.empty((B, T, Hv, 128), dtype=bf, device=dev)
     _check_tensor("output", o, bf, (B, T, Hv, 128), dev)
+    if checkpoint_every_n_tokens:
+        _require(state_checkpoints is not None and checkpoint_cu_starts is not None and
+                 checkpoint_cu_starts_cpu is not None,
+                 "checkpoints need state_checkpoints and checkpoint_cu_starts with its CPU mirror")
+        _require(state_checkpoints.dim() == 4, "state_checkpoints must be [C, Hv, 128, 128]")
+        _check_tensor("state_checkpoints", state_checkpoints, bf,
+                      (state_checkpoints.shape[0], Hv, 128, 128), dev)
+        _check_tensor("checkpoint_cu_starts", checkpoint_cu_starts, torch.int64, (N + 1,), dev)
     p = make_infer_problem(B, T, Hqk, Hv, N, P, cu_seqlens, cu_seqlens_cpu, scale,
                            use_qk_l2norm_in_kernel, use_gate_in_kernel, lower_bound, beta_is_logit,
-                           ssm_state_indices, ssm_state_indices_cpu, route)
+                           ssm_state_indices, ssm_state_indices_cpu, route,
+                           checkpoint_every_n_tokens,
+                           state_checkpoints if checkpoint_every_n_tokens else None,
+                           checkpoint_cu_starts if checkpoint_every_n_tokens else None,
+                           checkpoint_cu_starts_cpu if checkpoint_every_n_tokens else None)
     kda_infer(p, q, k, v, g, beta, A_log, dt_bias, initial_state, o)
+    if checkpoint_every_n_tokens:
+        return o, initial_state, state_checkpoints
     return o, initial_state

@@ -373,7 +373,6 @@ kda::FwdArgs make_fwd_args(const Prob& p, const PlanEntry* plan, const void* q, 
     a.num_tasks = (int)p.num_tasks;
     a.ck_every = p.ck;
     a.scale = p.scale;
-    a.seg_mode = -1;
     return a;
 }
 
@@ -678,8 +677,32 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
                              {ip->cu_seqlens, ip->cu_seqlens ? (size_t)(p.N + 1) * 8 : 0, "cu_seqlens"},
                              {ip->state_indices, ip->state_indices ? (size_t)p.N * 4 : 0,
                               "state_indices"}};
+    // state checkpoints
+    const int E = ip->checkpoint_every;
+    if (E == 0) {
+        if (ip->state_checkpoints || ip->checkpoint_rows || ip->checkpoint_cu_starts ||
+            ip->checkpoint_cu_starts_host)
+            return fail(KDA_ERR_ROUTE, "checkpoint fields given with checkpoint_every = 0");
+    } else {
+        if (E < 0 || E % kChunk != 0)
+            return fail(KDA_ERR_ROUTE, "checkpoint_every must be a positive multiple of 16 (got %d)", E);
+        if (!ip->state_checkpoints || !ip->checkpoint_cu_starts || !ip->checkpoint_cu_starts_host)
+            return fail(KDA_ERR_NULL_ARG, "checkpoints need state_checkpoints and both start arrays");
+        const int64_t* cs = ip->checkpoint_cu_starts_host;
+        if (cs[0] != 0) return fail(KDA_ERR_SEQLENS, "checkpoint_cu_starts must start at 0");
+        for (int n = 0; n < p.N; ++n)
+            if (cs[n + 1] - cs[n] != (p.len[n] + E - 1) / E)
+                return fail(KDA_ERR_SEQLENS, "sequence %d needs %lld checkpoint rows (starts give %lld)", n,
+                            (long long)((p.len[n] + E - 1) / E), (long long)(cs[n + 1] - cs[n]));
+        if (cs[p.N] > ip->checkpoint_rows)
+            return fail(KDA_ERR_SHAPE, "checkpoints need %lld rows (have %lld)", (long long)cs[p.N],
+                        (long long)ip->checkpoint_rows);
+        ins.push_back({ip->checkpoint_cu_starts, (size_t)(p.N + 1) * 8, "checkpoint_cu_starts"});
+    }
     const size_t pool_bytes = (size_t)ip->pool_slots * p.Hv * kStateElems * 2;
-    std::vector<Span> outs = {{o, tv, "o"}, {state_pool, pool_bytes, "state_pool"}};
+    const size_t ck_bytes = E ? (size_t)ip->checkpoint_rows * p.Hv * kStateElems * 2 : 0;
+    std::vector<Span> outs = {{o, tv, "o"}, {state_pool, pool_bytes, "state_pool"},
+                              {ip->state_checkpoints, ck_bytes, "state_checkpoints"}};
     s = check_overlap(outs, ins);
     if (s != KDA_OK) return s;
 
@@ -704,6 +727,9 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
     a.pool = (kda::bf16_t*)state_pool;
     a.pool_index = ip->state_indices;
     a.pool_slots = ip->pool_slots;
+    a.ckpt = E ? (kda::bf16_t*)ip->state_checkpoints : nullptr;
+    a.ckpt_start = ip->checkpoint_cu_starts;
+    a.ckpt_every = E ? E : 1;
     e = route == KDA_ROUTE_CHUNK ? kda::launch_fwd_chunk(a, stream) : kda::launch_infer_token(a, stream);
     if (e != hipSuccess) return hip_fail(e, "inference launch");
     return KDA_OK;

@@ -325,6 +325,19 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         // more chunks left keeps co-resident tasks abreast.
         set_prio_by_remaining(ce - ci, ce - cb);
         const int64_t rec = (rec0 + ci) * a.Hv + h;  // record index (rebuild only)
+        if constexpr (kInfer) {
+            // state checkpoint before token t0 (E is a multiple of the chunk)
+            if (a.ckpt != nullptr && (ci * CH) % a.ckpt_every == 0) {
+                bf16* dst = (bf16*)a.ckpt + ((a.ckpt_start[n] + (ci * CH) / a.ckpt_every) * a.Hv + h) * (int64_t)D * D;
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int vcol = 16 * (2 * wave + j) + cl;
+                        *(bf16x4*)(dst + vcol * D + 16 * kb + 4 * gq) = to_bf4(S[kb][j]);
+                    }
+            }
+        }
 
         __syncthreads();   // chunk ci's prefix sums, exp(gC) and beta are in LDS
         // ---- C: decay factors and the chunk's operands ----

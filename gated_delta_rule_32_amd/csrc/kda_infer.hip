@@ -15,7 +15,9 @@
 // (recurrence of page "flashinfer.kda_backward.recurrent_kda_backward",
 // description).  The next token's inputs are fetched while the current one
 // is processed.  With one token per sequence (decode) the kernel moves each
-// state slot once in and once out.
+// state slot once in and once out.  With state checkpoints every E tokens the
+// state before token j*E is also stored, rounded to BF16, to row j of the
+// sequence's checkpoint rows (parameter state_checkpoints).
 #include "kda_common.hpp"
 #include "kda_kernels.h"
 
@@ -82,9 +84,21 @@ __global__ __launch_bounds__(IT_THREADS) void infer_token_kernel(FwdArgs a) {
     };
     TokIn nxt;
     load(nxt, 0);
+    bf16* ck = a.ckpt != nullptr ? (bf16*)a.ckpt + (a.ckpt_start[n] * a.Hv + h) * (int64_t)D * D : nullptr;
+    const int64_t ck_stride = (int64_t)a.Hv * D * D;
     for (int t = 0; t < L; ++t) {
         const TokIn cur = nxt;
         load(nxt, min(t + 1, L - 1));
+        if (ck != nullptr && t % a.ckpt_every == 0) {
+            bf16* dst = ck + (t / a.ckpt_every) * ck_stride;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                bf16x8 x;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] = (bf16)S[j][i];
+                *(bf16x8*)(dst + (16 * j + rbase) * D + kofs) = x;
+            }
+        }
         float qn[8], kn[8], al[8];
         float ssq = 0.f, ssk = 0.f;
 #pragma unroll

@@ -44,9 +44,6 @@ struct FwdArgs {
     int num_tasks;
     int ck_every;           // tape interval (tokens), multiple of 16
     float scale;
-    // state rebuild mode: process only the tokens of tape segment `seg`
-    // (0 = from the initial state); -1 = whole sequence
-    int seg_mode;
     // Inference (infer_token_kernel): prologue options and the BF16 state
     // pool [pool_slots][Hv][128][128] read and written in place at slot
     // pool_index[n] (slot n when pool_index is null); s0, s_final and tape
@@ -57,6 +54,11 @@ struct FwdArgs {
     bf16_t* pool;
     const int32_t* pool_index;
     int64_t pool_slots;
+    // inference state checkpoints: the BF16 state before token j*ckpt_every
+    // of sequence n goes to row ckpt_start[n] + j of ckpt [rows][Hv][128][128]
+    bf16_t* ckpt;           // null: none
+    const int64_t* ckpt_start;
+    int ckpt_every;
 };
 
 struct BwdArgs {

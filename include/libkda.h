@@ -215,6 +215,14 @@ kda_status kda_bwd(const kda_problem* p,
  * smaller one overflows the chunk factors); KDA_ROUTE_AUTO (0) takes the
  * chunked kernel for the in-kernel gate with lower_bound >= -5 when some
  * sequence is longer than one token, else the token-serial one.
+ * State checkpoints (parameters state_checkpoints, checkpoint_cu_starts,
+ * checkpoint_every_n_tokens): with checkpoint_every = E > 0 (a multiple of
+ * 16), sequence n stores ceil(L_n / E) BF16 states [Hv][128][128] into rows
+ * checkpoint_cu_starts[n] ... of state_checkpoints ([checkpoint_rows][Hv]
+ * [128][128]): row j holds the state before token j*E, so the first is the
+ * initial state.  The starts are device INT64 [N+1] with a host mirror that
+ * is checked (first 0, each count ceil(L_n / E), last <= checkpoint_rows).
+ * With E = 0 the four checkpoint fields must be NULL / 0.
  * Asynchronous; capturable under the same condition as kda_fwd. */
 typedef struct {
     int32_t B;
@@ -233,6 +241,11 @@ typedef struct {
     int64_t pool_slots;
     const int32_t* state_indices;       /* device INT32 [N], or NULL */
     const int32_t* state_indices_host;  /* host INT32 [N] mirror, NULL iff state_indices is NULL */
+    int32_t checkpoint_every;           /* E: 0 (none) or a positive multiple of 16 */
+    void* state_checkpoints;            /* BF16 [checkpoint_rows][Hv][128][128], or NULL */
+    int64_t checkpoint_rows;
+    const int64_t* checkpoint_cu_starts;       /* device INT64 [N+1], or NULL */
+    const int64_t* checkpoint_cu_starts_host;  /* host mirror */
 } kda_infer_problem;
 
 kda_status kda_infer(const kda_infer_problem* p,

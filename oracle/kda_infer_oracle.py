@@ -17,7 +17,10 @@ Source: page "flashinfer.kda.recurrent_kda", parameters:
   * initial_state with ssm_state_indices: a value-first state pool
     [P, Hv, V, K] whose slot indices[n] holds sequence n's initial state and
     receives its final state in place; slots no sequence names are left as
-    they were.
+    they were;
+  * state_checkpoints with checkpoint_every_n_tokens E: per sequence,
+    ceil(L / E) states, row j being the state before token j*E (row 0 the
+    initial state), stored from the sequence's cumulative start on.
 The recurrence itself is kda_oracle.recurrence (decay, delta-rule update from
 the decayed state, read-out from the updated state).
 
@@ -58,12 +61,13 @@ def infer_prologue(q, k, g, beta, A_log_h, dt_bias_h, use_qk_l2norm=True,
 
 def infer_forward(q, k, v, g, beta, A_log, dt_bias, pool, lengths, packed, indices=None,
                   scale=None, use_qk_l2norm=True, use_gate_in_kernel=False, lower_bound=None,
-                  beta_is_logit=False):
+                  beta_is_logit=False, checkpoint_every=0):
     """Whole-problem inference forward. q, k [B,T,Hqk,d]; v, g [B,T,Hv,d];
     beta [B,T,Hv]; A_log [Hv] or None; dt_bias [Hv,d] or None; pool
     [P,Hv,d,d]; indices [N] or None (slot n).
 
-    Returns (o [B,T,Hv,d], new_pool [P,Hv,d,d]) in FP64."""
+    Returns (o [B,T,Hv,d], new_pool [P,Hv,d,d]) in FP64, and with
+    checkpoint_every = E > 0 also the checkpoints [sum ceil(L/E), Hv, d, d]."""
     scale = SCALE if scale is None else float(scale)
     Hqk, Hv = q.shape[2], v.shape[2]
     G = Hv // Hqk
@@ -73,6 +77,9 @@ def infer_forward(q, k, v, g, beta, A_log, dt_bias, pool, lengths, packed, indic
         raise ValueError("pool slots must be distinct")
     o = np.full(tuple(v.shape), np.nan)
     new_pool = _np64(pool).copy()
+    E = int(checkpoint_every)
+    starts = np.concatenate([[0], np.cumsum([-(-int(L) // E) for L in lengths])]) if E else None
+    ckpts = np.full((int(starts[-1]), Hv) + tuple(pool.shape[2:]), np.nan) if E else None
     for (n, b, t0, L) in _slices(lengths, packed):
         s = slice(t0, t0 + L)
         for h in range(Hv):
@@ -82,8 +89,13 @@ def infer_forward(q, k, v, g, beta, A_log, dt_bias, pool, lengths, packed, indic
                 None if A_log is None else float(A_log[h]),
                 None if dt_bias is None else _np64(dt_bias[h]),
                 use_qk_l2norm, use_gate_in_kernel, lower_bound, beta_is_logit)
-            on, Sn = recurrence(qn, kn, _np64(v[b, s, h]), alpha, bb,
-                                _np64(pool[idx[n], h]), scale)
+            on, Sn, states = recurrence(qn, kn, _np64(v[b, s, h]), alpha, bb,
+                                        _np64(pool[idx[n], h]), scale, keep_states=True)
             o[b, s, h] = on
             new_pool[idx[n], h] = Sn
+            if E:
+                for j in range(-(-L // E)):
+                    ckpts[starts[n] + j, h] = states[j * E]   # before token j*E
+    if E:
+        return o, new_pool, ckpts
     return o, new_pool

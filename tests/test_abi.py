@@ -246,3 +246,31 @@ def test_infer_rejections_before_device_work():
     assert call(prob(), o_ptr=pool + 64) == 7
     assert call(prob(), o_ptr=v) == 7
     assert call(prob(), pool_ptr=q + 2) == 7
+
+
+def test_infer_checkpoint_rejections():
+    """State checkpoints: interval, per-sequence counts and capacity are
+    checked on the host (page "flashinfer.kda.recurrent_kda", parameters
+    state_checkpoints, checkpoint_cu_starts, checkpoint_every_n_tokens)."""
+    lib = kda._lib
+    nb = 16 * 128 * 2
+    base = 0x10000000
+    q, k, v, g, beta = (base + i * nb for i in range(5))
+    pool, o = base + 64 * nb, base + 2000 * nb
+    ckbuf = torch.empty((3, 1, 128, 128), dtype=torch.bfloat16)   # host memory: never touched
+    cu = torch.tensor([0, 5, 40], dtype=torch.int64)             # lengths 5 and 35
+
+    def call(every, starts, rows=3):
+        p = kda.make_infer_problem(1, 40, 1, 1, 2, 2, cu, cu, checkpoint_every=every,
+                                   state_checkpoints=ckbuf[:rows] if rows else None,
+                                   checkpoint_cu_starts=starts, checkpoint_cu_starts_cpu=starts)
+        return lib.kda_infer(ctypes.byref(p), q, k, v, g, beta, None, None, pool, o, None)
+
+    good = torch.tensor([0, 1, 4], dtype=torch.int64)           # ceil(5/16)=1, ceil(35/16)=3
+    assert call(24, good) == 11                                  # not a multiple of 16
+    assert call(16, torch.tensor([0, 1, 3], dtype=torch.int64)) == 4   # wrong count
+    assert call(16, torch.tensor([1, 2, 5], dtype=torch.int64)) == 4   # not starting at 0
+    assert call(16, good, rows=3) == 2                           # 4 rows needed, 3 given
+    # checkpoint fields without an interval
+    p = kda.make_infer_problem(1, 40, 1, 1, 2, 2, cu, cu, state_checkpoints=ckbuf)
+    assert lib.kda_infer(ctypes.byref(p), q, k, v, g, beta, None, None, pool, o, None) == 11

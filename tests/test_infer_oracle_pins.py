@@ -17,6 +17,8 @@ ssm_state_indices).
   the epsilon (relative 5e-7).
 * Pool: slots named by the indices receive the final states, in place; all
   other slots are returned unchanged.
+* Checkpoints: row 0 of a sequence is its initial state, and row j equals
+  the final state of the same sequence cut after j*E tokens.
 """
 import math
 
@@ -129,3 +131,28 @@ def test_pool_slots_in_place_and_untouched():
         assert np.array_equal(new[s], fs2[n])
     with pytest.raises(ValueError):
         kio.infer_forward(q, k, v, g, beta, None, None, pool, lengths, packed=True, indices=[1, 1, 2])
+
+
+def test_checkpoints_are_prefix_states():
+    rng = np.random.default_rng(16)
+    lengths, Hv, E = [5, 16, 17, 40], 2, 16
+    T = sum(lengths)
+    q, k = _rand(rng, 1, T, 1, D), _rand(rng, 1, T, 1, D)
+    v, g = _rand(rng, 1, T, Hv, D), -rng.random((1, T, Hv, D))
+    beta = rng.random((1, T, Hv))
+    pool = _rand(rng, 4, Hv, D, D)
+    o, new, ck = kio.infer_forward(q, k, v, g, beta, None, None, pool, lengths, packed=True,
+                                   checkpoint_every=E)
+    counts = [-(-L // E) for L in lengths]
+    assert ck.shape[0] == sum(counts)
+    row, t0 = 0, 0
+    for n, L in enumerate(lengths):
+        assert np.array_equal(ck[row], pool[n])
+        for j in range(1, counts[n]):
+            cut = j * E
+            s = slice(t0, t0 + cut)
+            _, fs = kio.infer_forward(q[:, s], k[:, s], v[:, s], g[:, s], beta[:, s], None, None,
+                                      pool[n:n + 1], [cut], packed=True)
+            np.testing.assert_allclose(ck[row + j], fs[0], rtol=1e-12, atol=1e-12)
+        row += counts[n]
+        t0 += L

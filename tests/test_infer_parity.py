@@ -120,3 +120,39 @@ def test_infer_training_settings_match_training_forward(route):
     torch.cuda.synchronize()
     pu.report_and_check([("o", o_i.float().cpu().numpy(), o_t.float().cpu().numpy()),
                          ("final_state", pool.float().cpu().numpy(), fs_t.cpu().numpy())])
+
+
+@pytest.mark.parametrize("route,every", [("chunk", 16), ("chunk", 32), ("token", 16), ("token", 48)])
+def test_infer_state_checkpoints(route, every):
+    """State checkpoints (parameters state_checkpoints, checkpoint_cu_starts,
+    checkpoint_every_n_tokens): row j of a sequence holds its state before
+    token j*E; rows past the last start are not touched."""
+    import gated_delta_rule_32_amd as kda
+    problem = P([5, 16, 17, 40, 100], 1, 2, packed=True)
+    inp = workloads.make_infer_inputs(problem, 507, 7)
+    counts = [-(-L // every) for L in problem.lengths]
+    starts_cpu = torch.tensor([0] + list(np.cumsum(counts)), dtype=torch.int64)
+    print(f"[infer] checkpoints route={route} every={every} rows={int(starts_cpu[-1])}", flush=True)
+    dev = torch.device("cuda")
+    rows = int(starts_cpu[-1]) + 2
+    ck = torch.full((rows, problem.Hv, 128, 128), 7.0, dtype=torch.bfloat16, device=dev)
+    pool = inp.pool.to(dev)
+    o, _pool, ck_out = kda.recurrent_kda(
+        inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev),
+        initial_state=pool, cu_seqlens=inp.cu_seqlens.to(dev), cu_seqlens_cpu=inp.cu_seqlens,
+        ssm_state_indices=inp.indices.to(dev), ssm_state_indices_cpu=inp.indices,
+        state_checkpoints=ck, checkpoint_cu_starts=starts_cpu.to(dev),
+        checkpoint_cu_starts_cpu=starts_cpu, checkpoint_every_n_tokens=every, route=ROUTES[route])
+    torch.cuda.synchronize()
+    assert ck_out.data_ptr() == ck.data_ptr()
+    o_ref, pool_ref, ck_ref = kio.infer_forward(
+        inp.q, inp.k, inp.v, inp.g, inp.beta, None, None, inp.pool, problem.lengths, True,
+        indices=inp.indices.tolist(), checkpoint_every=every)
+    got = ck.float().cpu().numpy()
+    n_rows = int(starts_cpu[-1])
+    pu.report_and_check([("o", o.float().cpu().numpy(), o_ref),
+                         ("checkpoints", got[:n_rows], ck_ref)])
+    # row 0 of every sequence is its initial state, exactly
+    for n, s0 in enumerate(starts_cpu[:-1].tolist()):
+        assert np.array_equal(got[s0], inp.pool[int(inp.indices[n])].float().numpy())
+    assert (got[n_rows:] == 7.0).all()
