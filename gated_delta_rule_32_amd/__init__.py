@@ -68,6 +68,7 @@ class KdaInferProblem(ctypes.Structure):
         ("checkpoint_every", ctypes.c_int32), ("state_checkpoints", ctypes.c_void_p),
         ("checkpoint_rows", ctypes.c_int64), ("checkpoint_cu_starts", ctypes.c_void_p),
         ("checkpoint_cu_starts_host", ctypes.c_void_p),
+        ("num_spec_tokens", ctypes.c_int32), ("num_accepted_tokens", ctypes.c_void_p),
     ]
 
 
@@ -218,7 +219,9 @@ def make_infer_problem(B: int, T: int, Hqk: int, Hv: int, N: int, pool_slots: in
                        route: int = ROUTE_AUTO, checkpoint_every: int = 0,
                        state_checkpoints: Optional[torch.Tensor] = None,
                        checkpoint_cu_starts: Optional[torch.Tensor] = None,
-                       checkpoint_cu_starts_cpu: Optional[torch.Tensor] = None) -> KdaInferProblem:
+                       checkpoint_cu_starts_cpu: Optional[torch.Tensor] = None,
+                       num_spec_tokens: int = 0,
+                       num_accepted_tokens: Optional[torch.Tensor] = None) -> KdaInferProblem:
     p = KdaInferProblem()
     p.B, p.T, p.Hqk, p.Hv, p.N = int(B), int(T), int(Hqk), int(Hv), int(N)
     p.cu_seqlens = _ptr(cu_seqlens)
@@ -237,6 +240,8 @@ def make_infer_problem(B: int, T: int, Hqk: int, Hv: int, N: int, pool_slots: in
     p.checkpoint_rows = 0 if state_checkpoints is None else int(state_checkpoints.shape[0])
     p.checkpoint_cu_starts = _ptr(checkpoint_cu_starts)
     p.checkpoint_cu_starts_host = _ptr(checkpoint_cu_starts_cpu)
+    p.num_spec_tokens = int(num_spec_tokens)
+    p.num_accepted_tokens = _ptr(num_accepted_tokens)
     return p
 
 
@@ -383,6 +388,7 @@ def recurrent_kda_training_backward(context: RecurrentKDATrainingContext, do, df
 def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initial_state=None,
                   use_qk_l2norm_in_kernel: bool = True, use_gate_in_kernel: bool = False,
                   lower_bound=None, cu_seqlens=None, ssm_state_indices=None,
+                  num_spec_tokens: Optional[int] = None, num_accepted_tokens=None,
                   output=None, beta_is_logit: bool = False, state_checkpoints=None,
                   checkpoint_cu_starts=None, checkpoint_every_n_tokens: int = 0, *,
                   cu_seqlens_cpu=None, ssm_state_indices_cpu=None, checkpoint_cu_starts_cpu=None,
@@ -396,8 +402,11 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
     With checkpoint_every_n_tokens = E > 0, state_checkpoints (BF16
     [C, Hv, 128, 128]) receives, from row checkpoint_cu_starts[n] on, the
     states of sequence n before tokens 0, E, 2E, ... and the call returns
-    (output, initial_state, state_checkpoints).  Speculative decode and the
-    softplus gate are not supported."""
+    (output, initial_state, state_checkpoints).  Speculative decode
+    (num_spec_tokens = S): every sequence has 1+S tokens, ssm_state_indices is
+    [N, 1+S]; the state starts from slot [n, a-1] with a =
+    num_accepted_tokens[n] clamped to [1, 1+S] (1 when omitted) and the state
+    after token s goes to slot [n, s].  The softplus gate is not supported."""
     dev = q.device
     _require(q.dim() == 4 and v.dim() == 4, "q and v must be [B, T, H, 128]")
     B, T, Hqk, Dq = q.shape
@@ -430,9 +439,11 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
     if dt_bias is not None:
         dt_bias = dt_bias.reshape(Hv, 128) if dt_bias.dim() == 1 else dt_bias
         _check_tensor("dt_bias", dt_bias, torch.float32, (Hv, 128), dev)
+    S = int(num_spec_tokens or 0)
     if ssm_state_indices is not None:
         _require(ssm_state_indices_cpu is not None, "ssm_state_indices needs its CPU mirror")
-        _check_tensor("ssm_state_indices", ssm_state_indices, torch.int32, (N,), dev)
+        _check_tensor("ssm_state_indices", ssm_state_indices, torch.int32,
+                      (N, 1 + S) if S else (N,), dev)
         _require(ssm_state_indices_cpu.dtype == torch.int32 and
                  ssm_state_indices_cpu.device.type == "cpu" and ssm_state_indices_cpu.is_contiguous(),
                  "ssm_state_indices_cpu must be a contiguous int32 CPU tensor")
@@ -452,7 +463,10 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
                            checkpoint_every_n_tokens,
                            state_checkpoints if checkpoint_every_n_tokens else None,
                            checkpoint_cu_starts if checkpoint_every_n_tokens else None,
-                           checkpoint_cu_starts_cpu if checkpoint_every_n_tokens else None)
+                           checkpoint_cu_starts_cpu if checkpoint_every_n_tokens else None,
+                           S, num_accepted_tokens)
+    if num_accepted_tokens is not None:
+        _check_tensor("num_accepted_tokens", num_accepted_tokens, torch.int32, (N,), dev)
     kda_infer(p, q, k, v, g, beta, A_log, dt_bias, initial_state, o)
     if checkpoint_every_n_tokens:
         return o, initial_state, state_checkpoints

@@ -653,17 +653,35 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
         return fail(KDA_ERR_SHAPE, "pool_slots out of range (%lld)", (long long)ip->pool_slots);
     if ((ip->state_indices == nullptr) != (ip->state_indices_host == nullptr))
         return fail(KDA_ERR_NULL_ARG, "state_indices and state_indices_host go together");
+    // speculative decode: 1+S tokens and 1+S slots per sequence
+    const int S = ip->num_spec_tokens;
+    if (S < 0) return fail(KDA_ERR_SHAPE, "num_spec_tokens must be >= 0 (got %d)", S);
+    if (S == 0 && ip->num_accepted_tokens != nullptr)
+        return fail(KDA_ERR_SHAPE, "num_accepted_tokens needs num_spec_tokens > 0");
+    if (S > 0) {
+        if (ip->state_indices == nullptr)
+            return fail(KDA_ERR_NULL_ARG, "speculative decode needs state_indices [N][1+S]");
+        if (ip->checkpoint_every != 0)
+            return fail(KDA_ERR_ROUTE, "speculative decode takes no state checkpoints");
+        if (ip->route == KDA_ROUTE_CHUNK)
+            return fail(KDA_ERR_ROUTE, "speculative decode runs on the token-serial route");
+        for (int n = 0; n < p.N; ++n)
+            if (p.len[n] != 1 + S)
+                return fail(KDA_ERR_SEQLENS, "sequence %d has %lld tokens; speculative decode needs 1+S=%d",
+                            n, (long long)p.len[n], 1 + S);
+    }
+    const int64_t n_idx = (int64_t)p.N * (1 + S);
     if (ip->state_indices_host != nullptr) {
-        std::vector<int32_t> sorted(ip->state_indices_host, ip->state_indices_host + p.N);
-        for (int n = 0; n < p.N; ++n) {
-            const int32_t slot = sorted[n];
+        std::vector<int32_t> sorted(ip->state_indices_host, ip->state_indices_host + n_idx);
+        for (int64_t i = 0; i < n_idx; ++i) {
+            const int32_t slot = sorted[i];
             if (slot < 0 || slot >= ip->pool_slots)
-                return fail(KDA_ERR_SHAPE, "state_indices[%d] = %d is outside the pool", n, slot);
+                return fail(KDA_ERR_SHAPE, "state_indices[%lld] = %d is outside the pool", (long long)i, slot);
         }
         std::sort(sorted.begin(), sorted.end());
-        for (int n = 1; n < p.N; ++n)
-            if (sorted[n] == sorted[n - 1])
-                return fail(KDA_ERR_SHAPE, "pool slot %d is named twice", sorted[n]);
+        for (int64_t i = 1; i < n_idx; ++i)
+            if (sorted[i] == sorted[i - 1])
+                return fail(KDA_ERR_SHAPE, "pool slot %d is named twice", sorted[i]);
     } else if (ip->pool_slots < p.N) {
         return fail(KDA_ERR_SHAPE, "without state_indices the pool needs N=%d slots (has %lld)", p.N,
                     (long long)ip->pool_slots);
@@ -675,8 +693,10 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
                              {A_log, A_log ? (size_t)p.Hv * 4 : 0, "A_log"},
                              {dt_bias, dt_bias ? (size_t)p.Hv * D * 4 : 0, "dt_bias"},
                              {ip->cu_seqlens, ip->cu_seqlens ? (size_t)(p.N + 1) * 8 : 0, "cu_seqlens"},
-                             {ip->state_indices, ip->state_indices ? (size_t)p.N * 4 : 0,
-                              "state_indices"}};
+                             {ip->state_indices, ip->state_indices ? (size_t)n_idx * 4 : 0,
+                              "state_indices"},
+                             {ip->num_accepted_tokens, ip->num_accepted_tokens ? (size_t)p.N * 4 : 0,
+                              "num_accepted_tokens"}};
     // state checkpoints
     const int E = ip->checkpoint_every;
     if (E == 0) {
@@ -716,7 +736,7 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
     kda::FwdArgs a = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, nullptr);
     const int64_t longest = *std::max_element(p.len.begin(), p.len.end());
     const int route = ip->route != KDA_ROUTE_AUTO ? ip->route
-                      : (bounded_gate && longest > 1) ? KDA_ROUTE_CHUNK : KDA_ROUTE_ROWSPLIT;
+                      : (bounded_gate && longest > 1 && S == 0) ? KDA_ROUTE_CHUNK : KDA_ROUTE_ROWSPLIT;
     a.o = o;
     a.scale = scale;
     a.infer = 1;
@@ -730,6 +750,8 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
     a.ckpt = E ? (kda::bf16_t*)ip->state_checkpoints : nullptr;
     a.ckpt_start = ip->checkpoint_cu_starts;
     a.ckpt_every = E ? E : 1;
+    a.spec_tokens = S;
+    a.spec_accepted = ip->num_accepted_tokens;
     e = route == KDA_ROUTE_CHUNK ? kda::launch_fwd_chunk(a, stream) : kda::launch_infer_token(a, stream);
     if (e != hipSuccess) return hip_fail(e, "inference launch");
     return KDA_OK;

@@ -17,7 +17,11 @@
 // is processed.  With one token per sequence (decode) the kernel moves each
 // state slot once in and once out.  With state checkpoints every E tokens the
 // state before token j*E is also stored, rounded to BF16, to row j of the
-// sequence's checkpoint rows (parameter state_checkpoints).
+// sequence's checkpoint rows (parameter state_checkpoints).  Speculative
+// decode (parameters num_spec_tokens, num_accepted_tokens): the state starts
+// from the slot of the last accepted token of the previous round and is
+// written after every token to that token's own slot, so that the next round
+// can resume from any accepted prefix.
 #include "kda_common.hpp"
 #include "kda_kernels.h"
 
@@ -46,9 +50,17 @@ __global__ __launch_bounds__(IT_THREADS) void infer_token_kernel(FwdArgs a) {
     const int L = a.plan.seq_len[n];
     // pool slot of sequence n (checked on the host; a slot out of range ends
     // the workgroup before any access)
-    const int64_t slot = a.pool_index != nullptr ? a.pool_index[n] : n;
+    const int spec = a.spec_tokens;
+    int64_t slot;
+    if (spec > 0) {
+        const int acc = a.spec_accepted != nullptr ? a.spec_accepted[n] : 1;
+        slot = a.pool_index[(int64_t)n * (spec + 1) + min(max(acc, 1), spec + 1) - 1];
+    } else {
+        slot = a.pool_index != nullptr ? a.pool_index[n] : n;
+    }
     if (slot < 0 || slot >= a.pool_slots) return;
     bf16* pool = (bf16*)a.pool + (slot * a.Hv + h) * (int64_t)D * D;
+    const int64_t slab_elems = (int64_t)a.Hv * D * D;
 
     float S[8][8];
 #pragma unroll
@@ -146,13 +158,28 @@ __global__ __launch_bounds__(IT_THREADS) void infer_token_kernel(FwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) op[t * sv + 16 * j] = (bf16)(a.scale * ov[j]);
         }
+        if (spec > 0) {  // the state after token t, to token t's slot
+            const int64_t st = a.pool_index[(int64_t)n * (spec + 1) + t];
+            if (st >= 0 && st < a.pool_slots) {
+                bf16* dst = (bf16*)a.pool + st * slab_elems + h * (int64_t)D * D;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    bf16x8 x;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) x[i] = (bf16)S[j][i];
+                    *(bf16x8*)(dst + (16 * j + rbase) * D + kofs) = x;
+                }
+            }
+        }
     }
+    if (spec == 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        bf16x8 x;
+        for (int j = 0; j < 8; ++j) {
+            bf16x8 x;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = (bf16)S[j][i];
-        *(bf16x8*)(pool + (16 * j + rbase) * D + kofs) = x;
+            for (int i = 0; i < 8; ++i) x[i] = (bf16)S[j][i];
+            *(bf16x8*)(pool + (16 * j + rbase) * D + kofs) = x;
+        }
     }
 }
 

@@ -59,6 +59,11 @@ struct FwdArgs {
     bf16_t* ckpt;           // null: none
     const int64_t* ckpt_start;
     int ckpt_every;
+    // speculative decode (spec_tokens = S > 0): pool_index is [N][1+S]; the
+    // state is read from slot [n][a-1] (a = spec_accepted[n] clamped to
+    // [1, 1+S], 1 if null) and written after token s to slot [n][s]
+    int spec_tokens;
+    const int32_t* spec_accepted;
 };
 
 struct BwdArgs {

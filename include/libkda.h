@@ -223,6 +223,14 @@ kda_status kda_bwd(const kda_problem* p,
  * initial state.  The starts are device INT64 [N+1] with a host mirror that
  * is checked (first 0, each count ceil(L_n / E), last <= checkpoint_rows).
  * With E = 0 the four checkpoint fields must be NULL / 0.
+ * Speculative decode (parameters num_spec_tokens, num_accepted_tokens,
+ * ssm_state_indices [N, 1+S]): with num_spec_tokens = S > 0 every sequence
+ * has exactly 1+S tokens and state_indices holds 1+S distinct slots per
+ * sequence (row-major [N][1+S]).  The initial state is read from slot
+ * state_indices[n][a-1], a = num_accepted_tokens[n] clamped to [1, 1+S]
+ * (a = 1 when num_accepted_tokens is NULL), and the state after token s is
+ * written to slot state_indices[n][s].  Always the token-serial kernel; no
+ * checkpoints.
  * Asynchronous; capturable under the same condition as kda_fwd. */
 typedef struct {
     int32_t B;
@@ -246,6 +254,8 @@ typedef struct {
     int64_t checkpoint_rows;
     const int64_t* checkpoint_cu_starts;       /* device INT64 [N+1], or NULL */
     const int64_t* checkpoint_cu_starts_host;  /* host mirror */
+    int32_t num_spec_tokens;            /* S: 0 (plain decode / prefill) or > 0 */
+    const int32_t* num_accepted_tokens; /* device INT32 [N], or NULL */
 } kda_infer_problem;
 
 kda_status kda_infer(const kda_infer_problem* p,

@@ -20,7 +20,13 @@ Source: page "flashinfer.kda.recurrent_kda", parameters:
     they were;
   * state_checkpoints with checkpoint_every_n_tokens E: per sequence,
     ceil(L / E) states, row j being the state before token j*E (row 0 the
-    initial state), stored from the sequence's cumulative start on.
+    initial state), stored from the sequence's cumulative start on;
+  * num_spec_tokens S with ssm_state_indices [N, 1+S] and num_accepted_tokens:
+    every sequence has 1+S tokens; its initial state is slot [n, a-1], a the
+    accepted count of the previous round clamped to [1, 1+S] (slot [n, 0]
+    without counts), and the state after token s goes to slot [n, s]
+    (reading: the per-token slots are the checkpoints a later round resumes
+    from).
 The recurrence itself is kda_oracle.recurrence (decay, delta-rule update from
 the decayed state, read-out from the updated state).
 
@@ -61,7 +67,8 @@ def infer_prologue(q, k, g, beta, A_log_h, dt_bias_h, use_qk_l2norm=True,
 
 def infer_forward(q, k, v, g, beta, A_log, dt_bias, pool, lengths, packed, indices=None,
                   scale=None, use_qk_l2norm=True, use_gate_in_kernel=False, lower_bound=None,
-                  beta_is_logit=False, checkpoint_every=0):
+                  beta_is_logit=False, checkpoint_every=0, num_spec_tokens=0,
+                  num_accepted=None):
     """Whole-problem inference forward. q, k [B,T,Hqk,d]; v, g [B,T,Hv,d];
     beta [B,T,Hv]; A_log [Hv] or None; dt_bias [Hv,d] or None; pool
     [P,Hv,d,d]; indices [N] or None (slot n).
@@ -72,8 +79,18 @@ def infer_forward(q, k, v, g, beta, A_log, dt_bias, pool, lengths, packed, indic
     Hqk, Hv = q.shape[2], v.shape[2]
     G = Hv // Hqk
     N = len(lengths)
-    idx = list(range(N)) if indices is None else [int(i) for i in indices]
-    if len(set(idx)) != N:
+    S = int(num_spec_tokens)
+    if S:
+        slots = [[int(x) for x in row] for row in indices]
+        if any(int(L) != 1 + S for L in lengths):
+            raise ValueError("speculative decode needs 1+S tokens per sequence")
+        flat = [x for row in slots for x in row]
+        acc = [1] * N if num_accepted is None else [min(max(int(a), 1), 1 + S) for a in num_accepted]
+        idx = [slots[n][acc[n] - 1] for n in range(N)]
+    else:
+        idx = list(range(N)) if indices is None else [int(i) for i in indices]
+        flat = idx
+    if len(set(flat)) != len(flat):
         raise ValueError("pool slots must be distinct")
     o = np.full(tuple(v.shape), np.nan)
     new_pool = _np64(pool).copy()
@@ -92,7 +109,11 @@ def infer_forward(q, k, v, g, beta, A_log, dt_bias, pool, lengths, packed, indic
             on, Sn, states = recurrence(qn, kn, _np64(v[b, s, h]), alpha, bb,
                                         _np64(pool[idx[n], h]), scale, keep_states=True)
             o[b, s, h] = on
-            new_pool[idx[n], h] = Sn
+            if S:
+                for t in range(1 + S):
+                    new_pool[slots[n][t], h] = states[t + 1]   # after token t
+            else:
+                new_pool[idx[n], h] = Sn
             if E:
                 for j in range(-(-L // E)):
                     ckpts[starts[n] + j, h] = states[j * E]   # before token j*E

@@ -274,3 +274,30 @@ def test_infer_checkpoint_rejections():
     # checkpoint fields without an interval
     p = kda.make_infer_problem(1, 40, 1, 1, 2, 2, cu, cu, state_checkpoints=ckbuf)
     assert lib.kda_infer(ctypes.byref(p), q, k, v, g, beta, None, None, pool, o, None) == 11
+
+
+def test_infer_spec_decode_rejections():
+    """Speculative decode needs 1+S tokens and 1+S distinct slots per
+    sequence, the token-serial route and no checkpoints."""
+    lib = kda._lib
+    nb = 16 * 128 * 2
+    base = 0x10000000
+    q, k, v, g, beta = (base + i * nb for i in range(5))
+    pool, o = base + 64 * nb, base + 2000 * nb
+    cu = torch.tensor([0, 3, 6], dtype=torch.int64)              # two sequences of 3 tokens
+    idx = torch.tensor([0, 1, 2, 3, 4, 5], dtype=torch.int32)
+
+    def call(**kw):
+        base_kw = dict(state_indices=idx, state_indices_cpu=idx, num_spec_tokens=2)
+        base_kw.update(kw)
+        p = kda.make_infer_problem(1, 6, 1, 1, 2, 8, cu, cu, **base_kw)
+        return lib.kda_infer(ctypes.byref(p), q, k, v, g, beta, None, None, pool, o, None)
+
+    assert call(num_spec_tokens=3) == 4                          # sequences are not 1+S long
+    assert call(state_indices=None, state_indices_cpu=None) == 1
+    assert call(route=1) == 11
+    dup = torch.tensor([0, 1, 2, 3, 4, 0], dtype=torch.int32)
+    assert call(state_indices=dup, state_indices_cpu=dup) == 2
+    acc = torch.zeros(2, dtype=torch.int32)
+    assert call(num_spec_tokens=0, num_accepted_tokens=acc, state_indices=idx[:2],
+                state_indices_cpu=idx[:2]) == 2

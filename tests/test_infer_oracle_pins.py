@@ -19,6 +19,8 @@ ssm_state_indices).
   other slots are returned unchanged.
 * Checkpoints: row 0 of a sequence is its initial state, and row j equals
   the final state of the same sequence cut after j*E tokens.
+* Speculative decode: slot [n, s] receives the state after token s, equal to
+  a plain run over the first s+1 tokens from the accepted slot's state.
 """
 import math
 
@@ -156,3 +158,27 @@ def test_checkpoints_are_prefix_states():
             np.testing.assert_allclose(ck[row + j], fs[0], rtol=1e-12, atol=1e-12)
         row += counts[n]
         t0 += L
+
+
+def test_spec_decode_slots_are_prefix_states():
+    rng = np.random.default_rng(17)
+    N, S, Hv = 3, 2, 2
+    lengths = [1 + S] * N
+    T = sum(lengths)
+    q, k = _rand(rng, 1, T, 1, D), _rand(rng, 1, T, 1, D)
+    v, g = _rand(rng, 1, T, Hv, D), -rng.random((1, T, Hv, D))
+    beta = rng.random((1, T, Hv))
+    pool = _rand(rng, 10, Hv, D, D)
+    slots = [[4, 0, 7], [1, 9, 2], [3, 5, 6]]
+    acc = [2, 0, 9]                         # clamped to 2, 1 and 3
+    start_slot = [0, 1, 6]
+    o, new = kio.infer_forward(q, k, v, g, beta, None, None, pool, lengths, packed=True,
+                               indices=slots, num_spec_tokens=S, num_accepted=acc)
+    assert np.array_equal(new[8], pool[8])   # named by no sequence
+    for n in range(N):
+        for t in range(1 + S):
+            s = slice(n * (1 + S), n * (1 + S) + t + 1)
+            o1, fs = kio.infer_forward(q[:, s], k[:, s], v[:, s], g[:, s], beta[:, s], None, None,
+                                       pool[start_slot[n]:start_slot[n] + 1], [t + 1], packed=True)
+            np.testing.assert_allclose(new[slots[n][t]], fs[0], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(o[0, n * (1 + S) + t], o1[0, t], rtol=1e-12, atol=1e-12)

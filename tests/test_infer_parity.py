@@ -156,3 +156,40 @@ def test_infer_state_checkpoints(route, every):
     for n, s0 in enumerate(starts_cpu[:-1].tolist()):
         assert np.array_equal(got[s0], inp.pool[int(inp.indices[n])].float().numpy())
     assert (got[n_rows:] == 7.0).all()
+
+
+@pytest.mark.parametrize("accepted", ["given", "omitted"])
+@pytest.mark.parametrize("packed", [True, False])
+def test_infer_spec_decode(accepted, packed):
+    """Speculative decode (parameters num_spec_tokens, num_accepted_tokens,
+    ssm_state_indices [N, 1+S]): the state starts from the slot of the last
+    accepted token and the state after every token lands in that token's
+    slot."""
+    import gated_delta_rule_32_amd as kda
+    N, S, slots = 24, 3, 128
+    problem = P([1 + S] * N, 2, 4, packed=packed)
+    inp = workloads.make_infer_inputs(problem, 508, slots)
+    gen = torch.Generator().manual_seed(509)
+    idx_cpu = torch.randperm(slots, generator=gen)[:N * (1 + S)].to(torch.int32).reshape(N, 1 + S)
+    acc_cpu = torch.randint(0, 2 + S + 1, (N,), generator=gen, dtype=torch.int32)  # includes 0 and > 1+S
+    print(f"[infer] spec decode packed={packed} accepted={accepted}", flush=True)
+    dev = torch.device("cuda")
+    pool = inp.pool.to(dev)
+    o, _ = kda.recurrent_kda(
+        inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev),
+        initial_state=pool, cu_seqlens=None if inp.cu_seqlens is None else inp.cu_seqlens.to(dev),
+        cu_seqlens_cpu=inp.cu_seqlens, ssm_state_indices=idx_cpu.to(dev),
+        ssm_state_indices_cpu=idx_cpu, num_spec_tokens=S,
+        num_accepted_tokens=acc_cpu.to(dev) if accepted == "given" else None)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = kio.infer_forward(
+        inp.q, inp.k, inp.v, inp.g, inp.beta, None, None, inp.pool, problem.lengths, packed,
+        indices=idx_cpu.tolist(), num_spec_tokens=S,
+        num_accepted=acc_cpu.tolist() if accepted == "given" else None)
+    got = pool.float().cpu().numpy()
+    named = idx_cpu.flatten().tolist()
+    pu.report_and_check([("o", o.float().cpu().numpy(), o_ref),
+                         ("token_slots", got[named], pool_ref[named])])
+    before = inp.pool.float().numpy()
+    for s in set(range(slots)) - set(named):
+        assert np.array_equal(got[s], before[s])
