@@ -69,6 +69,8 @@ class KdaInferProblem(ctypes.Structure):
         ("checkpoint_rows", ctypes.c_int64), ("checkpoint_cu_starts", ctypes.c_void_p),
         ("checkpoint_cu_starts_host", ctypes.c_void_p),
         ("num_spec_tokens", ctypes.c_int32), ("num_accepted_tokens", ctypes.c_void_p),
+        ("state_source", ctypes.c_void_p), ("source_slots", ctypes.c_int64),
+        ("source_indices", ctypes.c_void_p), ("source_indices_host", ctypes.c_void_p),
     ]
 
 
@@ -221,7 +223,10 @@ def make_infer_problem(B: int, T: int, Hqk: int, Hv: int, N: int, pool_slots: in
                        checkpoint_cu_starts: Optional[torch.Tensor] = None,
                        checkpoint_cu_starts_cpu: Optional[torch.Tensor] = None,
                        num_spec_tokens: int = 0,
-                       num_accepted_tokens: Optional[torch.Tensor] = None) -> KdaInferProblem:
+                       num_accepted_tokens: Optional[torch.Tensor] = None,
+                       state_source: Optional[torch.Tensor] = None,
+                       source_indices: Optional[torch.Tensor] = None,
+                       source_indices_cpu: Optional[torch.Tensor] = None) -> KdaInferProblem:
     p = KdaInferProblem()
     p.B, p.T, p.Hqk, p.Hv, p.N = int(B), int(T), int(Hqk), int(Hv), int(N)
     p.cu_seqlens = _ptr(cu_seqlens)
@@ -242,6 +247,10 @@ def make_infer_problem(B: int, T: int, Hqk: int, Hv: int, N: int, pool_slots: in
     p.checkpoint_cu_starts_host = _ptr(checkpoint_cu_starts_cpu)
     p.num_spec_tokens = int(num_spec_tokens)
     p.num_accepted_tokens = _ptr(num_accepted_tokens)
+    p.state_source = _ptr(state_source)
+    p.source_slots = 0 if state_source is None else int(state_source.shape[0])
+    p.source_indices = _ptr(source_indices)
+    p.source_indices_host = _ptr(source_indices_cpu)
     return p
 
 
@@ -389,10 +398,11 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
                   use_qk_l2norm_in_kernel: bool = True, use_gate_in_kernel: bool = False,
                   lower_bound=None, cu_seqlens=None, ssm_state_indices=None,
                   num_spec_tokens: Optional[int] = None, num_accepted_tokens=None,
-                  output=None, beta_is_logit: bool = False, state_checkpoints=None,
+                  output=None, initial_state_source=None, initial_state_indices=None,
+                  beta_is_logit: bool = False, state_checkpoints=None,
                   checkpoint_cu_starts=None, checkpoint_every_n_tokens: int = 0, *,
                   cu_seqlens_cpu=None, ssm_state_indices_cpu=None, checkpoint_cu_starts_cpu=None,
-                  route: int = ROUTE_AUTO):
+                  initial_state_indices_cpu=None, route: int = ROUTE_AUTO):
     """Decode / prefill subset of page "flashinfer.kda.recurrent_kda": returns
     (output, initial_state) with initial_state, a BF16 state pool
     [P, Hv, 128, 128], updated in place (slot ssm_state_indices[n] for sequence
@@ -406,7 +416,9 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
     (num_spec_tokens = S): every sequence has 1+S tokens, ssm_state_indices is
     [N, 1+S]; the state starts from slot [n, a-1] with a =
     num_accepted_tokens[n] clamped to [1, 1+S] (1 when omitted) and the state
-    after token s goes to slot [n, s].  The softplus gate is not supported."""
+    after token s goes to slot [n, s].  initial_state_source (a read-only BF16
+    pool) with initial_state_indices [N] (and their CPU mirror) replaces the
+    state each sequence starts from.  The softplus gate is not supported."""
     dev = q.device
     _require(q.dim() == 4 and v.dim() == 4, "q and v must be [B, T, H, 128]")
     B, T, Hqk, Dq = q.shape
@@ -467,6 +479,17 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
                            S, num_accepted_tokens)
     if num_accepted_tokens is not None:
         _check_tensor("num_accepted_tokens", num_accepted_tokens, torch.int32, (N,), dev)
+    if initial_state_source is not None:
+        _require(initial_state_indices is not None and initial_state_indices_cpu is not None,
+                 "initial_state_source needs initial_state_indices and their CPU mirror")
+        _require(initial_state_source.dim() == 4, "initial_state_source must be [P0, Hv, 128, 128]")
+        _check_tensor("initial_state_source", initial_state_source, bf,
+                      (initial_state_source.shape[0], Hv, 128, 128), dev)
+        _check_tensor("initial_state_indices", initial_state_indices, torch.int32, (N,), dev)
+        p.state_source = _ptr(initial_state_source)
+        p.source_slots = int(initial_state_source.shape[0])
+        p.source_indices = _ptr(initial_state_indices)
+        p.source_indices_host = _ptr(initial_state_indices_cpu)
     kda_infer(p, q, k, v, g, beta, A_log, dt_bias, initial_state, o)
     if checkpoint_every_n_tokens:
         return o, initial_state, state_checkpoints

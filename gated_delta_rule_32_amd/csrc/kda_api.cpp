@@ -686,6 +686,19 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
         return fail(KDA_ERR_SHAPE, "without state_indices the pool needs N=%d slots (has %lld)", p.N,
                     (long long)ip->pool_slots);
     }
+    // read-only source pool
+    if ((ip->state_source == nullptr) != (ip->source_indices == nullptr) ||
+        (ip->source_indices == nullptr) != (ip->source_indices_host == nullptr))
+        return fail(KDA_ERR_NULL_ARG, "state_source, source_indices and its host mirror go together");
+    if (ip->state_source != nullptr) {
+        if (ip->source_slots < 1 ||
+            ip->source_slots > ((int64_t)1 << 40) / ((int64_t)p.Hv * kStateElems))
+            return fail(KDA_ERR_SHAPE, "source_slots out of range (%lld)", (long long)ip->source_slots);
+        for (int n = 0; n < p.N; ++n)
+            if (ip->source_indices_host[n] < 0 || ip->source_indices_host[n] >= ip->source_slots)
+                return fail(KDA_ERR_SHAPE, "source_indices[%d] = %d is outside the source pool", n,
+                            ip->source_indices_host[n]);
+    }
     const size_t tq = (size_t)p.tokens * p.Hqk * D * 2;
     const size_t tv = (size_t)p.tokens * p.Hv * D * 2;
     std::vector<Span> ins = {{q, tq, "q"}, {k, tq, "k"}, {v, tv, "v"}, {g, tv, "g"},
@@ -696,7 +709,12 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
                              {ip->state_indices, ip->state_indices ? (size_t)n_idx * 4 : 0,
                               "state_indices"},
                              {ip->num_accepted_tokens, ip->num_accepted_tokens ? (size_t)p.N * 4 : 0,
-                              "num_accepted_tokens"}};
+                              "num_accepted_tokens"},
+                             {ip->state_source,
+                              ip->state_source ? (size_t)ip->source_slots * p.Hv * kStateElems * 2 : 0,
+                              "state_source"},
+                             {ip->source_indices, ip->source_indices ? (size_t)p.N * 4 : 0,
+                              "source_indices"}};
     // state checkpoints
     const int E = ip->checkpoint_every;
     if (E == 0) {
@@ -752,6 +770,9 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
     a.ckpt_every = E ? E : 1;
     a.spec_tokens = S;
     a.spec_accepted = ip->num_accepted_tokens;
+    a.src_pool = (const kda::bf16_t*)ip->state_source;
+    a.src_index = ip->source_indices;
+    a.src_slots = ip->source_slots;
     e = route == KDA_ROUTE_CHUNK ? kda::launch_fwd_chunk(a, stream) : kda::launch_infer_token(a, stream);
     if (e != hipSuccess) return hip_fail(e, "inference launch");
     return KDA_OK;

@@ -173,10 +173,17 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     // inference: the pool slot of sequence n (checked on the host; a slot
     // out of range ends the workgroup before any access or barrier)
     bf16* pslab = nullptr;
+    const bf16* pinit = nullptr;  // initial state: the source pool's slot when given
     if constexpr (kInfer) {
         const int64_t slot = a.pool_index != nullptr ? a.pool_index[n] : n;
         if (slot < 0 || slot >= a.pool_slots) return;
         pslab = (bf16*)a.pool + (slot * a.Hv + h) * (int64_t)D * D;
+        pinit = pslab;
+        if (a.src_pool != nullptr) {
+            const int64_t ss = a.src_index[n];
+            if (ss < 0 || ss >= a.src_slots) return;
+            pinit = (const bf16*)a.src_pool + (ss * a.Hv + h) * (int64_t)D * D;
+        }
     }
 
     // state: S^T frags for kb = 0..7 and vb = 2*wave + {0, 1}
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             for (int j = 0; j < 2; ++j) {
                 const int vcol = 16 * (2 * wave + j) + cl;
                 if constexpr (kInfer) {
-                    S[kb][j] = from_bf4(*(const bf16x4*)(pslab + vcol * D + 16 * kb + 4 * gq));
+                    S[kb][j] = from_bf4(*(const bf16x4*)(pinit + vcol * D + 16 * kb + 4 * gq));
                 } else {
                     const float4 x = *(const float4*)(src + (int64_t)vcol * D + 16 * kb + 4 * gq);
                     S[kb][j] = f32x4{x.x, x.y, x.z, x.w};

@@ -61,11 +61,18 @@ __global__ __launch_bounds__(IT_THREADS) void infer_token_kernel(FwdArgs a) {
     if (slot < 0 || slot >= a.pool_slots) return;
     bf16* pool = (bf16*)a.pool + (slot * a.Hv + h) * (int64_t)D * D;
     const int64_t slab_elems = (int64_t)a.Hv * D * D;
+    // initial state: the source pool's slot when one is given
+    const bf16* init = pool;
+    if (a.src_pool != nullptr) {
+        const int64_t ss = a.src_index[n];
+        if (ss < 0 || ss >= a.src_slots) return;
+        init = (const bf16*)a.src_pool + (ss * a.Hv + h) * (int64_t)D * D;
+    }
 
     float S[8][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const bf16x8 x = *(const bf16x8*)(pool + (16 * j + rbase) * D + kofs);
+        const bf16x8 x = *(const bf16x8*)(init + (16 * j + rbase) * D + kofs);
 #pragma unroll
         for (int i = 0; i < 8; ++i) S[j][i] = (float)x[i];
     }

@@ -64,6 +64,11 @@ struct FwdArgs {
     // [1, 1+S], 1 if null) and written after token s to slot [n][s]
     int spec_tokens;
     const int32_t* spec_accepted;
+    // read-only source pool: when set, sequence n starts from its slot
+    // src_index[n] instead of its state-pool slot
+    const bf16_t* src_pool;
+    const int32_t* src_index;
+    int64_t src_slots;
 };
 
 struct BwdArgs {

@@ -231,6 +231,12 @@ kda_status kda_bwd(const kda_problem* p,
  * (a = 1 when num_accepted_tokens is NULL), and the state after token s is
  * written to slot state_indices[n][s].  Always the token-serial kernel; no
  * checkpoints.
+ * Read-only source pool (parameters initial_state_source,
+ * initial_state_indices): when state_source is given, sequence n starts from
+ * slot source_indices[n] of that BF16 pool [source_slots][Hv][128][128]
+ * instead of its slot in the state pool; the final (or per-token) states
+ * still go to the state pool.  Source slots may repeat; they are checked on
+ * the host mirror.
  * Asynchronous; capturable under the same condition as kda_fwd. */
 typedef struct {
     int32_t B;
@@ -256,6 +262,10 @@ typedef struct {
     const int64_t* checkpoint_cu_starts_host;  /* host mirror */
     int32_t num_spec_tokens;            /* S: 0 (plain decode / prefill) or > 0 */
     const int32_t* num_accepted_tokens; /* device INT32 [N], or NULL */
+    const void* state_source;           /* BF16 [source_slots][Hv][128][128], or NULL */
+    int64_t source_slots;
+    const int32_t* source_indices;      /* device INT32 [N], with state_source */
+    const int32_t* source_indices_host; /* host mirror */
 } kda_infer_problem;
 
 kda_status kda_infer(const kda_infer_problem* p,

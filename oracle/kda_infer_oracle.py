@@ -26,7 +26,9 @@ Source: page "flashinfer.kda.recurrent_kda", parameters:
     accepted count of the previous round clamped to [1, 1+S] (slot [n, 0]
     without counts), and the state after token s goes to slot [n, s]
     (reading: the per-token slots are the checkpoints a later round resumes
-    from).
+    from);
+  * initial_state_source with initial_state_indices: a read-only pool whose
+    slot source_indices[n] replaces the state sequence n starts from.
 The recurrence itself is kda_oracle.recurrence (decay, delta-rule update from
 the decayed state, read-out from the updated state).
 
@@ -68,7 +70,7 @@ def infer_prologue(q, k, g, beta, A_log_h, dt_bias_h, use_qk_l2norm=True,
 def infer_forward(q, k, v, g, beta, A_log, dt_bias, pool, lengths, packed, indices=None,
                   scale=None, use_qk_l2norm=True, use_gate_in_kernel=False, lower_bound=None,
                   beta_is_logit=False, checkpoint_every=0, num_spec_tokens=0,
-                  num_accepted=None):
+                  num_accepted=None, source=None, source_indices=None):
     """Whole-problem inference forward. q, k [B,T,Hqk,d]; v, g [B,T,Hv,d];
     beta [B,T,Hv]; A_log [Hv] or None; dt_bias [Hv,d] or None; pool
     [P,Hv,d,d]; indices [N] or None (slot n).
@@ -106,8 +108,9 @@ def infer_forward(q, k, v, g, beta, A_log, dt_bias, pool, lengths, packed, indic
                 None if A_log is None else float(A_log[h]),
                 None if dt_bias is None else _np64(dt_bias[h]),
                 use_qk_l2norm, use_gate_in_kernel, lower_bound, beta_is_logit)
-            on, Sn, states = recurrence(qn, kn, _np64(v[b, s, h]), alpha, bb,
-                                        _np64(pool[idx[n], h]), scale, keep_states=True)
+            S0 = _np64(pool[idx[n], h]) if source is None else _np64(source[int(source_indices[n]), h])
+            on, Sn, states = recurrence(qn, kn, _np64(v[b, s, h]), alpha, bb, S0, scale,
+                                        keep_states=True)
             o[b, s, h] = on
             if S:
                 for t in range(1 + S):

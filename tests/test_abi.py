@@ -301,3 +301,25 @@ def test_infer_spec_decode_rejections():
     acc = torch.zeros(2, dtype=torch.int32)
     assert call(num_spec_tokens=0, num_accepted_tokens=acc, state_indices=idx[:2],
                 state_indices_cpu=idx[:2]) == 2
+
+
+def test_infer_source_pool_rejections():
+    lib = kda._lib
+    nb = 16 * 128 * 2
+    base = 0x10000000
+    q, k, v, g, beta = (base + i * nb for i in range(5))
+    pool, o, srcp = base + 64 * nb, base + 2000 * nb, base + 3000 * nb
+    sidx = torch.tensor([0, 3], dtype=torch.int32)
+    cu = torch.tensor([0, 5, 16], dtype=torch.int64)
+
+    def call(src, idx_dev, idx_host, slots=2):
+        p = kda.make_infer_problem(1, 16, 1, 1, 2, 2, cu, cu)
+        p.state_source, p.source_slots = src, slots
+        p.source_indices = None if idx_dev is None else idx_dev.data_ptr()
+        p.source_indices_host = None if idx_host is None else idx_host.data_ptr()
+        return lib.kda_infer(ctypes.byref(p), q, k, v, g, beta, None, None, pool, o, None)
+
+    assert call(srcp, sidx, sidx) == 2                     # slot 3 outside 2 slots
+    assert call(srcp, None, None) == 1                     # source without indices
+    assert call(None, sidx, sidx) == 1                     # indices without source
+    assert call(pool + 16, sidx, sidx, slots=4) == 7      # source overlaps the state pool

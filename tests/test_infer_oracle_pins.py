@@ -21,6 +21,8 @@ ssm_state_indices).
   the final state of the same sequence cut after j*E tokens.
 * Speculative decode: slot [n, s] receives the state after token s, equal to
   a plain run over the first s+1 tokens from the accepted slot's state.
+* Source pool: starting from source slot j equals starting from a pool whose
+  slot holds the same state; the source itself is not written.
 """
 import math
 
@@ -182,3 +184,23 @@ def test_spec_decode_slots_are_prefix_states():
                                        pool[start_slot[n]:start_slot[n] + 1], [t + 1], packed=True)
             np.testing.assert_allclose(new[slots[n][t]], fs[0], rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(o[0, n * (1 + S) + t], o1[0, t], rtol=1e-12, atol=1e-12)
+
+
+def test_source_pool_replaces_initial_state():
+    rng = np.random.default_rng(18)
+    lengths, Hv = [4, 6], 2
+    T = sum(lengths)
+    q, k = _rand(rng, 1, T, 1, D), _rand(rng, 1, T, 1, D)
+    v, g = _rand(rng, 1, T, Hv, D), -rng.random((1, T, Hv, D))
+    beta = rng.random((1, T, Hv))
+    pool = _rand(rng, 3, Hv, D, D)
+    src = _rand(rng, 2, Hv, D, D)
+    src_copy = src.copy()
+    o, new = kio.infer_forward(q, k, v, g, beta, None, None, pool, lengths, packed=True,
+                               indices=[2, 0], source=src, source_indices=[1, 1])
+    staged = pool.copy()
+    staged[2], staged[0] = src[1], src[1]
+    o2, new2 = kio.infer_forward(q, k, v, g, beta, None, None, staged, lengths, packed=True,
+                                 indices=[2, 0])
+    assert np.array_equal(o, o2) and np.array_equal(new[[0, 2]], new2[[0, 2]])
+    assert np.array_equal(new[1], pool[1]) and np.array_equal(src, src_copy)

@@ -193,3 +193,37 @@ def test_infer_spec_decode(accepted, packed):
     before = inp.pool.float().numpy()
     for s in set(range(slots)) - set(named):
         assert np.array_equal(got[s], before[s])
+
+
+@pytest.mark.parametrize("route", list(ROUTES.keys()))
+def test_infer_source_pool(route):
+    """Read-only source pool (parameters initial_state_source,
+    initial_state_indices): sequences start from source slots (repeats
+    allowed), final states land in the state pool, the source is untouched."""
+    import gated_delta_rule_32_amd as kda
+    problem = P([3, 40, 17, 64], 1, 2, packed=True)
+    inp = workloads.make_infer_inputs(problem, 510, 6)
+    gen = torch.Generator().manual_seed(511)
+    src_cpu = (0.1 * torch.randn((3, problem.Hv, 128, 128), generator=gen)).to(torch.bfloat16)
+    sidx_cpu = torch.tensor([2, 0, 2, 1], dtype=torch.int32)
+    print(f"[infer] source pool route={route}", flush=True)
+    dev = torch.device("cuda")
+    pool, src = inp.pool.to(dev), src_cpu.to(dev)
+    o, _ = kda.recurrent_kda(
+        inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev),
+        initial_state=pool, cu_seqlens=inp.cu_seqlens.to(dev), cu_seqlens_cpu=inp.cu_seqlens,
+        ssm_state_indices=inp.indices.to(dev), ssm_state_indices_cpu=inp.indices,
+        initial_state_source=src, initial_state_indices=sidx_cpu.to(dev),
+        initial_state_indices_cpu=sidx_cpu, route=ROUTES[route])
+    torch.cuda.synchronize()
+    o_ref, pool_ref = kio.infer_forward(
+        inp.q, inp.k, inp.v, inp.g, inp.beta, None, None, inp.pool, problem.lengths, True,
+        indices=inp.indices.tolist(), source=src_cpu, source_indices=sidx_cpu.tolist())
+    named = inp.indices.tolist()
+    got = pool.float().cpu().numpy()
+    pu.report_and_check([("o", o.float().cpu().numpy(), o_ref),
+                         ("state_pool", got[named], pool_ref[named])])
+    assert torch.equal(src.cpu(), src_cpu)
+    before = inp.pool.float().numpy()
+    for s in set(range(6)) - set(named):
+        assert np.array_equal(got[s], before[s])
