@@ -257,15 +257,28 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                     s0f[vb][j] = *(const bf16x4*)at(s0p, ((kb0 + j) * 8 + vb) * 256 + lane * 4);
         }
         __syncthreads();
-        // ---- P2: prefix sums over the chunk's tokens ----
-        if (tix < D) {
-            float acc = 0.f;
+        // ---- P2: prefix sums over the chunk's tokens.  Every wave takes 32
+        // channels: lanes 0-31 sum rows 0-7, lanes 32-63 rows 8-15 and add the
+        // lower half's total, swapped across the wave's halves. ----
+        {
+            const int ch = 32 * wave + (lane & 31);
+            const bool upper = lane >= 32;
+            const int r0 = upper ? 8 : 0;
+            float x[8];
 #pragma unroll
-            for (int rr = 0; rr < CH; ++rr) {
-                acc += sm.lam[rr][tix];
-                sm.lam[rr][tix] = acc;
-            }
-            sm.gamc[tix] = __builtin_amdgcn_exp2f(acc);
+            for (int i = 0; i < 8; ++i) x[i] = sm.lam[r0 + i][ch];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) x[i] += x[i - 1];
+            // upper lanes receive the lower half's total in [0], lower lanes
+            // the upper half's in [1]
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[7]), __float_as_uint(x[7]),
+                                                             false, false);
+            const float other = __uint_as_float(upper ? sw[0] : sw[1]);
+            const float off = upper ? other : 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sm.lam[r0 + i][ch] = x[i] + off;
+            // both halves hold the chunk total: the pair stores the same value
+            sm.gamc[ch] = __builtin_amdgcn_exp2f(x[7] + other);
         }
         {
             const bf16* up = (const bf16*)a.rec_u + rec * REC_U;
