@@ -103,3 +103,45 @@ def test_capture_without_cached_schedule_is_refused():
     step.run()
     torch.cuda.synchronize()
     assert np.isfinite(step.o.float().cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("route", [1, 2])
+def test_captured_inference_replays_match_eager(route):
+    """kda_infer under capture: every replay, started from the same pool
+    contents, must reproduce the eager call bit for bit (the pool is updated
+    in place, so it is restored before each replay)."""
+    import gated_delta_rule_32_amd as kda
+    problem = P([1, 9, 33, 16], 1, 2, packed=True)
+    inp = workloads.make_infer_inputs(problem, 404 + route, 6)
+    print(f"[graph] inference route={route}", flush=True)
+    dev = torch.device("cuda")
+    t = [x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta)]
+    cu, idx = inp.cu_seqlens.to(dev), inp.indices.to(dev)
+    pool0 = inp.pool.to(dev)
+    pool = pool0.clone()
+    o = torch.empty_like(t[2])
+    prob = kda.make_infer_problem(1, problem.T, problem.Hqk, problem.Hv, problem.N, 6, cu,
+                                  inp.cu_seqlens, state_indices=idx, state_indices_cpu=inp.indices,
+                                  route=route)
+
+    def run():
+        kda.kda_infer(prob, *t, None, None, pool, o, torch.cuda.current_stream().cuda_stream)
+    for _ in range(2):                      # make the schedule, then see it settled
+        pool.copy_(pool0)
+        run()
+        torch.cuda.synchronize()
+    eager_o, eager_pool = o.clone(), pool.clone()
+    graph = torch.cuda.CUDAGraph()
+    pool.copy_(pool0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        pool.copy_(pool0)
+        o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eager_o), f"replay {rep}: output differs"
+        assert torch.equal(pool, eager_pool), f"replay {rep}: pool differs"
