@@ -726,6 +726,9 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
             return fail(KDA_ERR_ROUTE, "checkpoint_every must be a positive multiple of 16 (got %d)", E);
         if (!ip->state_checkpoints || !ip->checkpoint_cu_starts || !ip->checkpoint_cu_starts_host)
             return fail(KDA_ERR_NULL_ARG, "checkpoints need state_checkpoints and both start arrays");
+        if (ip->checkpoint_rows < 1 ||
+            ip->checkpoint_rows > ((int64_t)1 << 40) / ((int64_t)p.Hv * kStateElems))
+            return fail(KDA_ERR_SHAPE, "checkpoint_rows out of range (%lld)", (long long)ip->checkpoint_rows);
         const int64_t* cs = ip->checkpoint_cu_starts_host;
         if (cs[0] != 0) return fail(KDA_ERR_SEQLENS, "checkpoint_cu_starts must start at 0");
         for (int n = 0; n < p.N; ++n)
