@@ -129,14 +129,17 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], 
 // log-space gate as given, beta as a logit or as given).  The chunk form
 // needs every per-token log-decay at or above -5 (so that the factors
 // exp(+-gc) stay in range); the host routes other calls elsewhere.
-constexpr int kFwdTape = 0, kFwdRebuild = 1, kFwdRecords = 2, kFwdInfer = 3;
+// kFwdInferCkpt is the same with state checkpoints (a separate instance, so
+// that the plain one keeps its registers).
+constexpr int kFwdTape = 0, kFwdRebuild = 1, kFwdRecords = 2, kFwdInfer = 3, kFwdInferCkpt = 4;
 
 template <int kMode>
 __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     constexpr bool kRebuild = kMode == kFwdRebuild;  // one segment, no output
     constexpr bool kOut = kMode != kFwdRebuild;      // o and the final state
     constexpr bool kRec = kMode == kFwdRebuild || kMode == kFwdRecords;  // per-chunk records
-    constexpr bool kInfer = kMode == kFwdInfer;      // BF16 pool state, prologue options
+    constexpr bool kInfer = kMode == kFwdInfer || kMode == kFwdInferCkpt;  // BF16 pool state, options
+    constexpr bool kCkpt = kMode == kFwdInferCkpt;   // state checkpoints
     __shared__ FwdLds sm;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -332,9 +335,9 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         // more chunks left keeps co-resident tasks abreast.
         set_prio_by_remaining(ce - ci, ce - cb);
         const int64_t rec = (rec0 + ci) * a.Hv + h;  // record index (rebuild only)
-        if constexpr (kInfer) {
+        if constexpr (kCkpt) {
             // state checkpoint before token t0 (E is a multiple of the chunk)
-            if (a.ckpt != nullptr && (ci * CH) % a.ckpt_every == 0) {
+            if ((ci * CH) % a.ckpt_every == 0) {
                 bf16* dst = (bf16*)a.ckpt + ((a.ckpt_start[n] + (ci * CH) / a.ckpt_every) * a.Hv + h) * (int64_t)D * D;
 #pragma unroll
                 for (int kb = 0; kb < 8; ++kb)
@@ -618,7 +621,10 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s) {
     if (a.num_tasks == 0) return hipSuccess;
-    if (a.infer)
+    if (a.infer && a.ckpt != nullptr)
+        hipLaunchKernelGGL(fwd_chunk_kernel<kFwdInferCkpt>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS),
+                           0, s, a);
+    else if (a.infer)
         hipLaunchKernelGGL(fwd_chunk_kernel<kFwdInfer>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0,
                            s, a);
     else if (a.rec_s0 != nullptr)
