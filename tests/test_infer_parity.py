@@ -227,3 +227,94 @@ def test_infer_source_pool(route):
     before = inp.pool.float().numpy()
     for s in set(range(6)) - set(named):
         assert np.array_equal(got[s], before[s])
+
+
+def _infer_task(inp_like, n, h, s0_task, **opts):
+    """Oracle of one (sequence, head) task of an inference call started from
+    s0_task [128, 128]: its output rows and final state (FP64)."""
+    p = inp_like["problem"]
+    sl = workloads.sequence_slices(p)[n]
+    _, b, t0, L = sl
+    s = slice(t0, t0 + L)
+    hq = h // (p.Hv // p.Hqk)
+    pick = lambda x, hh: x[b:b + 1, s, hh:hh + 1]
+    o, pool = kio.infer_forward(pick(inp_like["q"], hq), pick(inp_like["k"], hq),
+                                pick(inp_like["v"], h), pick(inp_like["g"], h),
+                                inp_like["beta"][b:b + 1, s, h:h + 1],
+                                None if inp_like["A_log"] is None else inp_like["A_log"][h:h + 1],
+                                None if inp_like["dt_bias"] is None else inp_like["dt_bias"][h:h + 1],
+                                s0_task[None, None], [L], True, **opts)
+    return o[0, :, 0], pool[0, 0], (b, t0, L)
+
+
+def test_infer_decode_bench_shape_sampled():
+    """The benchmark's decode step (256 one-token sequences, 96 heads, a
+    shuffled 256-slot pool) on the automatic route; sampled tasks against the
+    oracle, every output finite."""
+    import gated_delta_rule_32_amd as kda
+    problem = P([1] * 256, 96, 96, packed=True)
+    inp = workloads.make_infer_inputs(problem, 512, 256)
+    print("[infer] decode at the benchmark shape", flush=True)
+    dev = torch.device("cuda")
+    pool = inp.pool.to(dev)
+    o, _ = kda.recurrent_kda(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev),
+                             inp.beta.to(dev), initial_state=pool, cu_seqlens=inp.cu_seqlens.to(dev),
+                             cu_seqlens_cpu=inp.cu_seqlens, ssm_state_indices=inp.indices.to(dev),
+                             ssm_state_indices_cpu=inp.indices)
+    torch.cuda.synchronize()
+    o_np = o.float().cpu().numpy()
+    assert np.isfinite(o_np).all()
+    for (n, h) in [(0, 0), (100, 47), (255, 95)]:
+        slot = int(inp.indices[n])
+        ref_o, ref_s, (b, t0, L) = _infer_task(
+            dict(problem=problem, q=inp.q, k=inp.k, v=inp.v, g=inp.g, beta=inp.beta, A_log=None,
+                 dt_bias=None), n, h, inp.pool[slot, h])
+        pu.assert_close(f"o[{n},{h}]", o_np[b, t0:t0 + L, h], ref_o)
+        pu.assert_close(f"pool[{slot},{h}]", pool[slot, h].float().cpu().numpy(), ref_s)
+
+
+@pytest.mark.parametrize("route", list(ROUTES.keys()))
+def test_infer_prefill_packed_sampled(route):
+    """The packed workload (8 x 1024 tokens, 96 heads) through kda_infer with
+    the training settings, pool = initial states in BF16; sampled tasks
+    against the oracle."""
+    import gated_delta_rule_32_amd as kda
+    inp = workloads.make_workload("packed", with_adjoints=False)
+    problem = inp.problem
+    s0_bf = inp.initial_state.to(torch.bfloat16)
+    print(f"[infer] packed prefill route={route}", flush=True)
+    d = inp.to("cuda")
+    pool = s0_bf.to("cuda")
+    o, _ = kda.recurrent_kda(d.q, d.k, d.v, d.g, d.beta, A_log=d.A_log, dt_bias=d.dt_bias,
+                             initial_state=pool, use_gate_in_kernel=True, lower_bound=-5.0,
+                             beta_is_logit=True, cu_seqlens=d.cu_seqlens,
+                             cu_seqlens_cpu=inp.cu_seqlens, route=ROUTES[route])
+    torch.cuda.synchronize()
+    o_np = o.float().cpu().numpy()
+    assert np.isfinite(o_np).all()
+    for (n, h) in [(0, 0), (4, 48), (7, 95)]:
+        ref_o, ref_s, (b, t0, L) = _infer_task(
+            dict(problem=problem, q=inp.q, k=inp.k, v=inp.v, g=inp.g, beta=inp.beta, A_log=inp.A_log,
+                 dt_bias=inp.dt_bias), n, h, s0_bf[n, h],
+            use_gate_in_kernel=True, lower_bound=-5.0, beta_is_logit=True)
+        pu.assert_close(f"o[{n},{h}]", o_np[b, t0:t0 + L, h], ref_o)
+        pu.assert_close(f"pool[{n},{h}]", pool[n, h].float().cpu().numpy(), ref_s)
+
+
+@pytest.mark.parametrize("route", list(ROUTES.keys()))
+def test_infer_long_single_sequence(route):
+    """One 4096-token sequence (one task per head) on either route."""
+    import gated_delta_rule_32_amd as kda
+    problem = P([4096], 1, 2, packed=True)
+    inp = workloads.make_infer_inputs(problem, 513, 1)
+    print(f"[infer] 4096-token sequence route={route}", flush=True)
+    dev = torch.device("cuda")
+    pool = inp.pool.to(dev)
+    o, _ = kda.recurrent_kda(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev),
+                             inp.beta.to(dev), initial_state=pool, cu_seqlens=inp.cu_seqlens.to(dev),
+                             cu_seqlens_cpu=inp.cu_seqlens, route=ROUTES[route])
+    torch.cuda.synchronize()
+    o_ref, pool_ref = kio.infer_forward(inp.q, inp.k, inp.v, inp.g, inp.beta, None, None, inp.pool,
+                                        problem.lengths, True)
+    pu.report_and_check([("o", o.float().cpu().numpy(), o_ref),
+                         ("state_pool", pool.float().cpu().numpy(), pool_ref)])
