@@ -133,6 +133,9 @@ def main():
                          "sustained clocks before the warm-up and timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain copies of 1 GiB (counter calibration)")
+    ap.add_argument("--infer-only", action="store_true",
+                    help="only time kda_infer (decode and prefill) on the packed workload's heads, "
+                         "for per-kernel profiles of the inference routes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
@@ -152,6 +155,9 @@ def main():
     d = inp_cpu.to("cuda")
     dev = torch.device("cuda")
     stream = torch.cuda.current_stream()
+    if args.infer_only:
+        print(json.dumps({"inference": inference_steps(kda, p, d, inp_cpu, args, stream)}), flush=True)
+        return
     prob = kda.make_problem(p.B, p.T, p.Hqk, p.Hv, p.N, d.cu_seqlens, inp_cpu.cu_seqlens,
                             route=args.route)
     route, ntasks, _ = kda.kda_plan_query(prob)
