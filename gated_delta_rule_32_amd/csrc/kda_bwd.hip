@@ -57,9 +57,9 @@ struct BwdLds {
     alignas(16) float lam[CH][D];     // log2-domain decays, then their in-chunk prefix sums
     alignas(16) float gamc[D];        // exp(gC) per channel
     alignas(16) float dtz[D];         // dt_bias * exp(A_log) * log2(e)
-    alignas(16) float beta[CH];
-    alignas(16) float rqn[CH];        // 1/|q| and 1/|k| per token (0 past the end)
-    alignas(16) float rkn[CH];
+    alignas(16) float beta[2][CH];    // by chunk parity: the next chunk's are formed
+    alignas(16) float rqn[2][CH];     // during this one's last phase; 1/|q| and 1/|k|
+    alignas(16) float rkn[2][CH];     // per token (0 past the end)
     alignas(16) float dba[CH];        // dbeta contribution of dM.Akk
     alignas(16) float ta[3][CH][CH];  // T^T, Akk^T, Aqk'
     alignas(16) float dgc[D];         // dgC from the state part, per channel
@@ -189,6 +189,45 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     RowIn cur;
     load_row(cur, min((nchunks - 1) * CH + (tid >> 4), L - 1), (tid & 15) * 8);
     __syncthreads();
+    // ---- P1 of chunk ci: norms, gate, beta (row-owner mapping) from the
+    // rows in `cur`.  Run for chunk ci-1 in chunk ci's last phase (it writes
+    // only lam, which that phase no longer reads, and the other parity's
+    // beta and norms), and for the first chunk before the loop. ----
+    auto p1 = [&](const int ci) __attribute__((always_inline)) {
+        int tix = tid;
+        asm volatile("" : "+v"(tix));
+        const int r = tix >> 4;
+        const int c8 = (tix & 15) * 8;
+        const bool valid_r = r < L - ci * CH;
+        {
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {  // BF16 pair dot products, FP32 sums
+                const bf16x2 q2 = {cur.q[i], cur.q[i + 1]}, k2 = {cur.k[i], cur.k[i + 1]};
+                sq = __builtin_amdgcn_fdot2_f32_bf16(q2, q2, sq, false);
+                sk = __builtin_amdgcn_fdot2_f32_bf16(k2, k2, sk, false);
+            }
+            sq = row16_sum(sq);
+            sk = row16_sum(sk);
+            float lv[8], dz[8];
+            *(float4*)&dz[0] = *(const float4*)&sm.dtz[c8];
+            *(float4*)&dz[4] = *(const float4*)&sm.dtz[c8 + 4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float e = __builtin_amdgcn_exp2f(-((float)cur.g[i] * zs + dz[i]));
+                lv[i] = valid_r ? (-5.0f * LOG2E) * __builtin_amdgcn_rcpf(1.0f + e) : 0.f;
+            }
+            *(float4*)&sm.lam[r][c8] = make_float4(lv[0], lv[1], lv[2], lv[3]);
+            *(float4*)&sm.lam[r][c8 + 4] = make_float4(lv[4], lv[5], lv[6], lv[7]);
+            if ((tix & 15) == 0) {
+                sm.beta[ci & 1][r] = valid_r ? sigmoidf_((float)cur.b) : 0.f;
+                sm.rqn[ci & 1][r] = valid_r ? fast_rsqrt(sq + 1e-6f) : 0.f;
+                sm.rkn[ci & 1][r] = valid_r ? fast_rsqrt(sk + 1e-6f) : 0.f;
+            }
+        }
+    };
+    p1(nchunks - 1);
+    __syncthreads();
 
     auto chunk = [&](const int ci, auto tail_tag) __attribute__((always_inline)) {
         constexpr bool kTail = decltype(tail_tag)::value;
@@ -218,36 +257,10 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         if (tix < REC_TA / 4) ta4 = *(const float4*)at(a.rec_ta + rec * REC_TA, 4 * tix);
         bf16x4 s0f[8][2], ru[8], rdo[8];
 
-        // ---- P1: norms, gate, beta (row-owner mapping); stage T, Akk, Aqk ----
-        {
-            float sq = 0.f, sk = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {  // BF16 pair dot products, FP32 sums
-                const bf16x2 q2 = {cur.q[i], cur.q[i + 1]}, k2 = {cur.k[i], cur.k[i + 1]};
-                sq = __builtin_amdgcn_fdot2_f32_bf16(q2, q2, sq, false);
-                sk = __builtin_amdgcn_fdot2_f32_bf16(k2, k2, sk, false);
-            }
-            sq = row16_sum(sq);
-            sk = row16_sum(sk);
-            float lv[8], dz[8];
-            *(float4*)&dz[0] = *(const float4*)&sm.dtz[c8];
-            *(float4*)&dz[4] = *(const float4*)&sm.dtz[c8 + 4];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float e = __builtin_amdgcn_exp2f(-((float)cur.g[i] * zs + dz[i]));
-                lv[i] = valid_r ? (-5.0f * LOG2E) * __builtin_amdgcn_rcpf(1.0f + e) : 0.f;
-            }
-            *(float4*)&sm.lam[r][c8] = make_float4(lv[0], lv[1], lv[2], lv[3]);
-            *(float4*)&sm.lam[r][c8 + 4] = make_float4(lv[4], lv[5], lv[6], lv[7]);
-            if ((tix & 15) == 0) {
-                sm.beta[r] = valid_r ? sigmoidf_((float)cur.b) : 0.f;
-                sm.rqn[r] = valid_r ? fast_rsqrt(sq + 1e-6f) : 0.f;
-                sm.rkn[r] = valid_r ? fast_rsqrt(sk + 1e-6f) : 0.f;
-            }
-        }
-        // The state-side loads are spread over P1 and P2, each batch after
-        // the phase's arithmetic: a wave's loads queue at the memory pipeline
-        // and would otherwise hold back the in-order issue of that work.
+        // The state-side loads are spread over the chunk's first two phases
+        // (a wave's loads queue at the memory pipeline and would otherwise
+        // hold back the in-order issue of later work).  The chunk's P1 ran in
+        // the previous chunk's last phase; its barrier published it.
         {
             const bf16* s0p = (const bf16*)a.rec_s0 + rec * REC_S0;  // uniform record base
 #pragma unroll
@@ -256,7 +269,6 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 for (int j = 0; j < 2; ++j)
                     s0f[vb][j] = *(const bf16x4*)at(s0p, ((kb0 + j) * 8 + vb) * 256 + lane * 4);
         }
-        __syncthreads();
         // ---- P2: prefix sums over the chunk's tokens.  Every wave takes 32
         // channels: lanes 0-31 sum rows 0-7, lanes 32-63 rows 8-15 and add the
         // lower half's total, swapped across the wave's halves. ----
@@ -296,8 +308,8 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             *(float4*)&gc[4] = *(const float4*)&sm.lam[r][c8 + 4];
             *(float4*)&gC[0] = *(const float4*)&sm.gamc[c8];
             *(float4*)&gC[4] = *(const float4*)&sm.gamc[c8 + 4];
-            const float rq = sm.rqn[r] * scale;
-            const float rk = sm.rkn[r];
+            const float rq = sm.rqn[ci & 1][r] * scale;
+            const float rk = sm.rkn[ci & 1][r];
             bf16x4 qh4[2], ql4[2], kg4[2], kih4[2], kil4[2], kt4[2];
 #pragma unroll
             for (int s4 = 0; s4 < 2; ++s4) {
@@ -450,7 +462,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 *(bf16x4*)&sm.cf_du[vbo * FS + lane * 4] = cfdu;
                 // dBv^T = dU^T T (RF orientation): lane (gq, c) holds (T^T dU)[c][16vbo + 4gq + i]
                 const f32x4 dbvT = mma16(cfdu, tBb, zero4());
-                const float bc = sm.beta[cl];
+                const float bc = sm.beta[ci & 1][cl];
                 const f32x4 vvf = from_bf4(vv[jj]);
                 if (valid_c)
                     *(bf16x4*)at(dvp, ov + 16 * vbo + 4 * gq) = to_bf4(dbvT * bc);
@@ -485,7 +497,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             // dT += dW (beta Kg)^T over this wave's channels
             bf16x4 bk[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bk[j] = to_bf4(from_bf4(ld4(&sm.rf_kg[(kb0 + j) * FS], lane)) * sm.beta[cl]);
+            for (int j = 0; j < 2; ++j) bk[j] = to_bf4(from_bf4(ld4(&sm.rf_kg[(kb0 + j) * FS], lane)) * sm.beta[ci & 1][cl]);
             dT = mma32(cat8(dWb[0], dWb[1]), cat8(bk[0], bk[1]), dT);
             float* dTp = (float*)&sm.part[0][0][0][0];  // [4 waves][16 c][16 j]
 #pragma unroll
@@ -495,7 +507,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             f32x4 wcf[2];
             f32x4 tbA;  // frag(Tb^T): lane (gq, c) holds T[c][4gq+i] beta_{4gq+i}
 #pragma unroll
-            for (int i = 0; i < 4; ++i) tbA[i] = sm.ta[0][4 * gq + i][cl] * sm.beta[4 * gq + i];
+            for (int i = 0; i < 4; ++i) tbA[i] = sm.ta[0][4 * gq + i][cl] * sm.beta[ci & 1][4 * gq + i];
             const bf16x4 tbAb = to_bf4(tbA);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -504,7 +516,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 const f32x4 kgr = from_bf4(ld4(&sm.rf_kg[(kb0 + j) * FS], lane));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dbk += dbkT[i] * kgr[i];
-                dKgT[j] = dbkT * sm.beta[cl];
+                dKgT[j] = dbkT * sm.beta[ci & 1][cl];
                 // W = Tb Kg (CF): lane (gq, k) holds W[4gq + i][k]
                 wcf[j] = mma16(tbAb, ld4(&sm.cf_kg[(kb0 + j) * FS], lane), zero4());
             }
@@ -546,7 +558,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             float dba[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                dAkk[i] = (4 * gq + i > cl) ? sm.beta[4 * gq + i] * dM[i] : 0.f;
+                dAkk[i] = (4 * gq + i > cl) ? sm.beta[ci & 1][4 * gq + i] * dM[i] : 0.f;
                 dba[i] = row16_sum(dM[i] * akk[i]);
             }
             if (wave == 0 && cl == 0) {
@@ -570,7 +582,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         // per-element gradients (lane (gq, c), channels k = 16kb + 4gq + i)
         f32x4 qn4[2], kn4[2], dqn4[2], dkn4[2], dlam4[2], zl4[2];
         {
-            const float rq = sm.rqn[cl], rk = sm.rkn[cl];
+            const float rq = sm.rqn[ci & 1][cl], rk = sm.rkn[ci & 1][cl];
             float dotq = 0.f, dotk = 0.f;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -619,7 +631,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
 
         // ---- A3: prologue chain rule and stores ----
         {
-            const float rq = sm.rqn[cl], rk = sm.rkn[cl];
+            const float rq = sm.rqn[ci & 1][cl], rk = sm.rkn[ci & 1][cl];
             const float dotq = sm.dots[0][0][cl] + sm.dots[1][0][cl] + sm.dots[2][0][cl] + sm.dots[3][0][cl];
             const float dotk = sm.dots[0][1][cl] + sm.dots[1][1][cl] + sm.dots[2][1][cl] + sm.dots[3][1][cl];
 #pragma unroll
@@ -654,11 +666,12 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 const float db = sm.dbp[0][0][cl] + sm.dbp[0][1][cl] + sm.dbp[0][2][cl] + sm.dbp[0][3][cl] +
                                  sm.dbp[1][0][cl] + sm.dbp[1][1][cl] + sm.dbp[1][2][cl] + sm.dbp[1][3][cl] +
                                  sm.dba[cl];
-                const float bt = sm.beta[cl];
+                const float bt = sm.beta[ci & 1][cl];
                 // dbeta on the logit: db * sigma'(x) = db * beta (1 - beta)
                 *at(dbetap, __umul24(tc, sb)) = (bf16)(db * bt * (1.0f - bt));
             }
         }
+        if (ci > 0) p1(ci - 1);
         __syncthreads();
     };
     if (nfull < nchunks) chunk(nfull, std::true_type{});
