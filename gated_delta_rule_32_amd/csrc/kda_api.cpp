@@ -175,13 +175,92 @@ struct PlanEntry {
     void* host = nullptr;
     hipEvent_t ready = nullptr;
     bool settled = false;  // the upload behind `ready` was seen complete
+    bool pinned = false;   // used under stream capture: a graph holds its device pointers
+    int busy = 0;          // calls between get_plan and the end of their lease
+    uint64_t last = 0;     // least-recently-used order
+    // the last use on each stream that launched with it (events recorded
+    // after the launches; all complete means no queued kernel reads it)
+    std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
     size_t off_task = 0, off_start = 0, off_len = 0, off_tape = 0, off_chunk = 0, off_seg = 0;
     size_t bytes = 0;
 };
 
 std::mutex g_mu;
 std::map<std::vector<int64_t>, std::unique_ptr<PlanEntry>> g_plans;
-constexpr size_t kMaxPlans = 4096;
+uint64_t g_tick = 0;
+// Distinct length sets kept at once; when full, the least recently used
+// quarter of the evictable schedules is freed (variable-length training
+// makes a new set almost every step).
+constexpr size_t kMaxPlans = 1024;
+
+// Frees a schedule's buffers and events (null members are skipped).
+void free_plan(PlanEntry* e) {
+    for (auto& u : e->uses) hipEventDestroy(u.second);
+    e->uses.clear();
+    if (e->ready) hipEventDestroy(e->ready);
+    if (e->dev) hipFree(e->dev);
+    if (e->host) hipHostFree(e->host);
+    e->ready = nullptr;
+    e->dev = e->host = nullptr;
+}
+
+// Called with g_mu held when the cache is full.  A schedule may be freed only
+// when no call holds it, no captured graph refers to it, and its upload and
+// every launch that read it have completed (waited for here).
+kda_status evict_plans() {
+    using It = decltype(g_plans)::iterator;
+    std::vector<std::pair<uint64_t, It>> cand;
+    for (It it = g_plans.begin(); it != g_plans.end(); ++it)
+        if (it->second->busy == 0 && !it->second->pinned) cand.emplace_back(it->second->last, it);
+    if (cand.empty())
+        return fail(KDA_ERR_HIP, "schedule cache full (%zu length sets, all in use or captured)",
+                    g_plans.size());
+    std::sort(cand.begin(), cand.end(),
+              [](const std::pair<uint64_t, It>& x, const std::pair<uint64_t, It>& y) { return x.first < y.first; });
+    const size_t n = std::max<size_t>(1, cand.size() / 4);
+    for (size_t i = 0; i < n; ++i) {
+        PlanEntry* e = cand[i].second->second.get();
+        hipError_t r = hipEventSynchronize(e->ready);
+        for (size_t j = 0; r == hipSuccess && j < e->uses.size(); ++j) r = hipEventSynchronize(e->uses[j].second);
+        if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize(schedule eviction)");
+        free_plan(e);
+        g_plans.erase(cand[i].second);
+    }
+    return KDA_OK;
+}
+
+// One call's hold on a schedule, from get_plan to the end of the call: the
+// schedule cannot be evicted meanwhile, and at the end the call's last use is
+// recorded on its stream (or, for a call recorded into a graph, the schedule
+// is pinned for the life of the process).
+struct PlanLease {
+    PlanEntry* ent = nullptr;
+    hipStream_t stream = nullptr;
+    bool capturing = false;
+    PlanLease() = default;
+    PlanLease(const PlanLease&) = delete;
+    PlanLease& operator=(const PlanLease&) = delete;
+    ~PlanLease() {
+        if (ent == nullptr) return;
+        std::lock_guard<std::mutex> lock(g_mu);
+        --ent->busy;
+        if (capturing) {
+            ent->pinned = true;
+            return;
+        }
+        hipEvent_t ev = nullptr;
+        for (auto& u : ent->uses)
+            if (u.first == stream) ev = u.second;
+        if (ev == nullptr) {
+            if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+                ent->pinned = true;  // no way to know when it is free: keep it
+                return;
+            }
+            ent->uses.emplace_back(stream, ev);
+        }
+        if (hipEventRecord(ev, stream) != hipSuccess) ent->pinned = true;
+    }
+};
 
 std::vector<int64_t> plan_key(const Prob& p, int dev) {
     std::vector<int64_t> key = {dev, p.Hv, p.ck, p.packed ? 1 : 0, p.T, p.N};
@@ -192,7 +271,7 @@ std::vector<int64_t> plan_key(const Prob& p, int dev) {
 // Under stream capture only a settled cached schedule is usable: the call then
 // enqueues nothing but its kernels.  Outside capture a cached schedule whose
 // upload is still in flight is waited for on the caller's stream.
-kda_status get_plan(const Prob& p, hipStream_t stream, int dev, const PlanEntry** out) {
+kda_status get_plan(const Prob& p, hipStream_t stream, int dev, PlanLease& lease) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(stream, &cs);
     if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
@@ -217,15 +296,26 @@ kda_status get_plan(const Prob& p, hipStream_t stream, int dev, const PlanEntry*
             e = hipStreamWaitEvent(stream, ent->ready, 0);
             if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
         }
-        *out = ent;
+        ent->last = ++g_tick;
+        ++ent->busy;
+        lease.ent = ent;
+        lease.stream = stream;
+        lease.capturing = capturing;
         return KDA_OK;
     }
     if (capturing)
         return fail(KDA_ERR_CAPTURE,
                     "no schedule cached for these lengths; make the first call outside capture");
-    if (g_plans.size() >= kMaxPlans)
-        return fail(KDA_ERR_HIP, "schedule cache full (%zu distinct length sets)", g_plans.size());
+    if (g_plans.size() >= kMaxPlans) {
+        kda_status es = evict_plans();
+        if (es != KDA_OK) return es;
+    }
     auto ent = std::make_unique<PlanEntry>();
+    // on a failure below, free what was made so far
+    struct Guard {
+        std::unique_ptr<PlanEntry>& e;
+        ~Guard() { if (e) free_plan(e.get()); }
+    } guard{ent};
     size_t off = 0;
     ent->off_task = off;  off = align256(off + sizeof(int32_t) * (size_t)p.num_tasks);
     ent->off_start = off; off = align256(off + sizeof(int64_t) * (size_t)p.N);
@@ -273,8 +363,12 @@ kda_status get_plan(const Prob& p, hipStream_t stream, int dev, const PlanEntry*
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
     e = hipEventRecord(ent->ready, stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    *out = ent.get();
-    g_plans.emplace(std::move(key), std::move(ent));
+    ent->last = ++g_tick;
+    ent->busy = 1;
+    lease.ent = ent.get();
+    lease.stream = stream;
+    lease.capturing = false;
+    g_plans.emplace(std::move(key), std::move(ent));  // leaves `ent` empty: the guard frees nothing
     return KDA_OK;
 }
 
@@ -298,8 +392,13 @@ struct CtxRecord {
     const void* ptrs[8];
     hipStream_t stream;
     size_t ctx_bytes;
+    uint64_t seq;               // fill order
 };
 std::map<const void*, CtxRecord> g_ctx;
+uint64_t g_ctx_seq = 0;
+// Context buffers remembered at once; past that, filling a new buffer forgets
+// the one filled longest ago (its backward then reports a mismatch).
+constexpr size_t kMaxCtx = 4096;
 
 size_t tape_bytes(const Prob& p) {
     return (size_t)p.total_ck * (size_t)p.Hv * (size_t)kStateElems * sizeof(float);
@@ -485,9 +584,10 @@ kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const vo
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    const PlanEntry* plan = nullptr;
-    s = get_plan(p, stream, dev, &plan);
+    PlanLease lease;
+    s = get_plan(p, stream, dev, lease);
     if (s != KDA_OK) return s;
+    const PlanEntry* plan = lease.ent;
 
     kda::FwdArgs a = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, initial_state);
     a.o = o;
@@ -513,6 +613,13 @@ kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const vo
         r.stream = stream;
         r.ctx_bytes = ctx_bytes;
         std::lock_guard<std::mutex> lock(g_mu);
+        r.seq = ++g_ctx_seq;
+        if (g_ctx.size() >= kMaxCtx && g_ctx.find(ctx) == g_ctx.end()) {
+            auto oldest = g_ctx.begin();
+            for (auto it = g_ctx.begin(); it != g_ctx.end(); ++it)
+                if (it->second.seq < oldest->second.seq) oldest = it;
+            g_ctx.erase(oldest);
+        }
         g_ctx[ctx] = r;
     }
     return KDA_OK;
@@ -573,9 +680,10 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
     s = check_overlap(outs, ins);
     if (s != KDA_OK) return s;
 
-    const PlanEntry* plan = nullptr;
-    s = get_plan(p, stream, dev, &plan);
+    PlanLease lease;
+    s = get_plan(p, stream, dev, lease);
     if (s != KDA_OK) return s;
+    const PlanEntry* plan = lease.ent;
 
     kda::BwdArgs b{};
     b.f = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, initial_state);
@@ -751,9 +859,10 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    const PlanEntry* plan = nullptr;
-    s = get_plan(p, stream, dev, &plan);
+    PlanLease lease;
+    s = get_plan(p, stream, dev, lease);
     if (s != KDA_OK) return s;
+    const PlanEntry* plan = lease.ent;
     kda::FwdArgs a = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, nullptr);
     const int64_t longest = *std::max_element(p.len.begin(), p.len.end());
     const int route = ip->route != KDA_ROUTE_AUTO ? ip->route

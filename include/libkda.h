@@ -36,17 +36,23 @@
  * be a multiple of Hqk.  scale is 1/sqrt(128) and lower_bound is -5.
  *
  * Ownership.  The caller owns every buffer: inputs, outputs, the forward
- * context and the backward workspace.  The library keeps, per device, a cache
- * of small device-side schedules keyed by the sequence lengths (as the pages
+ * context and the backward workspace.  The library keeps a cache of small
+ * device-side schedules keyed by device and sequence lengths (as the pages
  * cache their longest-first order per unchanged offsets), and a host-side
- * record of each context's producing call for the backward's checks.
+ * record of each context's producing call for the backward's checks.  The
+ * cache holds at most 1024 schedules.  When a call needs a new one and the
+ * cache is full, the least recently used quarter of the schedules that no
+ * call holds and no captured graph uses is freed.  That call first waits on
+ * the host for the launches that last read them.  The context records keep
+ * the last 4096 contexts filled; a backward on a context forgotten since
+ * returns KDA_ERR_CTX_MISMATCH.
  *
  * Errors.  Every entry point returns a kda_status.  All argument checks run on
  * the host before any launch; nothing is launched when a check fails.  A HIP
  * failure after launches began returns KDA_ERR_HIP; kda_last_error() gives
  * the text of the last failure on the calling thread.  Launches are
  * asynchronous on the given stream (a hipStream_t; NULL is the null stream).
- * No entry point synchronises the device.
+ * No entry point synchronises the device, except the schedule eviction above.
  *
  * Stream capture.  kda_fwd and kda_bwd may be recorded into a HIP graph: under
  * capture they enqueue kernel launches only (no allocation, copy, memset or
