@@ -152,6 +152,8 @@ def make_problem(B: int, T: int, Hqk: int, Hv: int, N: int,
     p.route = int(route)
     p.checkpoint_every = int(checkpoint_every)
     p.context = int(context)
+    # the struct holds raw pointers: keep the tensors alive with it
+    p._keep = (cu_seqlens, cu_seqlens_cpu)
     return p
 
 
@@ -251,6 +253,10 @@ def make_infer_problem(B: int, T: int, Hqk: int, Hv: int, N: int, pool_slots: in
     p.source_slots = 0 if state_source is None else int(state_source.shape[0])
     p.source_indices = _ptr(source_indices)
     p.source_indices_host = _ptr(source_indices_cpu)
+    # the struct holds raw pointers: keep the tensors alive with it
+    p._keep = (cu_seqlens, cu_seqlens_cpu, state_indices, state_indices_cpu, state_checkpoints,
+               checkpoint_cu_starts, checkpoint_cu_starts_cpu, num_accepted_tokens, state_source,
+               source_indices, source_indices_cpu)
     return p
 
 

@@ -323,3 +323,27 @@ def test_infer_source_pool_rejections():
     assert call(srcp, None, None) == 1                     # source without indices
     assert call(None, sidx, sidx) == 1                     # indices without source
     assert call(pool + 16, sidx, sidx, slots=4) == 7      # source overlaps the state pool
+
+
+def test_problem_keeps_its_offsets_alive():
+    """The problem structs hold raw pointers to cu_seqlens and the other index
+    tensors: they keep those tensors alive, so a problem made in a helper is
+    still valid after the helper's tensors went out of scope."""
+    import gc
+
+    def make():
+        cu = torch.tensor([0, 3, 40, 41], dtype=torch.int64)
+        return kda.make_problem(1, 41, 1, 2, 3, cu, cu.clone())
+
+    p = make()
+    gc.collect()
+    junk = [torch.full((4,), -7, dtype=torch.int64) for _ in range(256)]  # reuse freed memory
+    route, ntasks, order = kda.kda_plan_query(p, with_order=True)
+    assert ntasks == 6 and order[:2] == [2, 3]   # sequence 1 (37 tokens) first
+    del junk
+    ip = kda.make_infer_problem(1, 41, 1, 2, 3, 8, torch.tensor([0, 3, 40, 41], dtype=torch.int64),
+                                torch.tensor([0, 3, 40, 41], dtype=torch.int64),
+                                state_indices=torch.tensor([5, 1, 2], dtype=torch.int32),
+                                state_indices_cpu=torch.tensor([5, 1, 2], dtype=torch.int32))
+    gc.collect()
+    assert all(t is not None for t in ip._keep[:4])
