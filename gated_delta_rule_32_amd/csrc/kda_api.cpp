@@ -879,6 +879,7 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
     a.pool_slots = ip->pool_slots;
     a.ckpt = E ? (kda::bf16_t*)ip->state_checkpoints : nullptr;
     a.ckpt_start = ip->checkpoint_cu_starts;
+    a.ckpt_rows = E ? ip->checkpoint_rows : 0;
     a.ckpt_every = E ? E : 1;
     a.spec_tokens = S;
     a.spec_accepted = ip->num_accepted_tokens;

@@ -337,8 +337,12 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         const int64_t rec = (rec0 + ci) * a.Hv + h;  // record index (rebuild only)
         if constexpr (kCkpt) {
             // state checkpoint before token t0 (E is a multiple of the chunk)
-            if ((ci * CH) % a.ckpt_every == 0) {
-                bf16* dst = (bf16*)a.ckpt + ((a.ckpt_start[n] + (ci * CH) / a.ckpt_every) * a.Hv + h) * (int64_t)D * D;
+            // (the row comes from the caller's device copy of the starts, which
+            // the host checked only through its mirror: a row out of range is
+            // skipped rather than stored)
+            const int64_t row = a.ckpt_start[n] + (ci * CH) / a.ckpt_every;
+            if ((ci * CH) % a.ckpt_every == 0 && row >= 0 && row < a.ckpt_rows) {
+                bf16* dst = (bf16*)a.ckpt + (row * a.Hv + h) * (int64_t)D * D;
 #pragma unroll
                 for (int kb = 0; kb < 8; ++kb)
 #pragma unroll

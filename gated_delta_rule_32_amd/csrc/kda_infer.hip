@@ -103,12 +103,15 @@ __global__ __launch_bounds__(IT_THREADS) void infer_token_kernel(FwdArgs a) {
     };
     TokIn nxt;
     load(nxt, 0);
-    bf16* ck = a.ckpt != nullptr ? (bf16*)a.ckpt + (a.ckpt_start[n] * a.Hv + h) * (int64_t)D * D : nullptr;
+    // checkpoint rows start at the caller's device copy of the starts, which
+    // the host checked only through its mirror: rows out of range are skipped
+    const int64_t ck_row0 = a.ckpt != nullptr ? a.ckpt_start[n] : 0;
+    bf16* ck = a.ckpt != nullptr && ck_row0 >= 0 ? (bf16*)a.ckpt + (ck_row0 * a.Hv + h) * (int64_t)D * D : nullptr;
     const int64_t ck_stride = (int64_t)a.Hv * D * D;
     for (int t = 0; t < L; ++t) {
         const TokIn cur = nxt;
         load(nxt, min(t + 1, L - 1));
-        if (ck != nullptr && t % a.ckpt_every == 0) {
+        if (ck != nullptr && t % a.ckpt_every == 0 && ck_row0 + t / a.ckpt_every < a.ckpt_rows) {
             bf16* dst = ck + (t / a.ckpt_every) * ck_stride;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {

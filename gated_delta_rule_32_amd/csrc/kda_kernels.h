@@ -58,6 +58,7 @@ struct FwdArgs {
     // of sequence n goes to row ckpt_start[n] + j of ckpt [rows][Hv][128][128]
     bf16_t* ckpt;           // null: none
     const int64_t* ckpt_start;
+    int64_t ckpt_rows;      // rows of ckpt; a row outside [0, ckpt_rows) is not stored
     int ckpt_every;
     // speculative decode (spec_tokens = S > 0): pool_index is [N][1+S]; the
     // state is read from slot [n][a-1] (a = spec_accepted[n] clamped to

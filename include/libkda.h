@@ -228,6 +228,8 @@ kda_status kda_bwd(const kda_problem* p,
  * [128][128]): row j holds the state before token j*E, so the first is the
  * initial state.  The starts are device INT64 [N+1] with a host mirror that
  * is checked (first 0, each count ceil(L_n / E), last <= checkpoint_rows).
+ * The kernels read the device copy; a row it places outside
+ * [0, checkpoint_rows) is not stored.
  * With E = 0 the four checkpoint fields must be NULL / 0.
  * Speculative decode (parameters num_spec_tokens, num_accepted_tokens,
  * ssm_state_indices [N, 1+S]): with num_spec_tokens = S > 0 every sequence

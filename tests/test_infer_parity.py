@@ -158,6 +158,39 @@ def test_infer_state_checkpoints(route, every):
     assert (got[n_rows:] == 7.0).all()
 
 
+@pytest.mark.parametrize("route", ["chunk", "token"])
+def test_infer_checkpoint_rows_out_of_range_are_skipped(route):
+    """The kernels read the checkpoint starts from the caller's device copy,
+    which the host checks only through its mirror.  When the device copy
+    names rows past the end (here every start + 1000, and one negative), no
+    checkpoint row is stored, and the outputs and the pool are as without
+    checkpoints."""
+    import gated_delta_rule_32_amd as kda
+    every = 16
+    problem = P([5, 16, 40], 1, 2, packed=True)
+    inp = workloads.make_infer_inputs(problem, 517, 5)
+    counts = [-(-L // every) for L in problem.lengths]
+    starts_cpu = torch.tensor([0] + list(np.cumsum(counts)), dtype=torch.int64)
+    bad = starts_cpu + 1000
+    bad[1] = -3
+    print(f"[infer] checkpoint rows out of range route={route}", flush=True)
+    dev = torch.device("cuda")
+    rows = int(starts_cpu[-1])
+    ck = torch.full((rows, problem.Hv, 128, 128), 7.0, dtype=torch.bfloat16, device=dev)
+    args = (inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev))
+    kw = dict(cu_seqlens=inp.cu_seqlens.to(dev), cu_seqlens_cpu=inp.cu_seqlens,
+              ssm_state_indices=inp.indices.to(dev), ssm_state_indices_cpu=inp.indices,
+              route=ROUTES[route])
+    pool_a, pool_b = inp.pool.to(dev), inp.pool.to(dev)
+    o_a, _, _ = kda.recurrent_kda(*args, initial_state=pool_a, state_checkpoints=ck,
+                                  checkpoint_cu_starts=bad.to(dev), checkpoint_cu_starts_cpu=starts_cpu,
+                                  checkpoint_every_n_tokens=every, **kw)
+    o_b, _ = kda.recurrent_kda(*args, initial_state=pool_b, **kw)
+    torch.cuda.synchronize()
+    assert (ck.float() == 7.0).all()
+    assert torch.equal(o_a, o_b) and torch.equal(pool_a, pool_b)
+
+
 @pytest.mark.parametrize("accepted", ["given", "omitted"])
 @pytest.mark.parametrize("packed", [True, False])
 def test_infer_spec_decode(accepted, packed):
