@@ -35,6 +35,12 @@ FWD_SOURCES = ["gated_delta_rule_32_amd/csrc/kda_fwd_chunk.hip",
                "gated_delta_rule_32_amd/csrc/kda_kernels.h"]
 
 
+ROUTE_NAMES = {1: "chunk", 2: "rowsplit", 3: "segments"}
+ROUTE_KERNELS = {1: "fwd_chunk_kernel", 2: "fwd_rowsplit_kernel",
+                 3: "fwd_chunk_kernel over all tape segments (P and Q, seg_combine_kernel, rerun): "
+                    "the whole forward's time"}
+
+
 def fwd_source_sha() -> str:
     import hashlib
     h = hashlib.sha256()
@@ -224,7 +230,7 @@ def main():
     traffic = recorded_traffic() if (route == 1 and p.name == "packed") else None
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "fwd_chunk_kernel" if route == 1 else "fwd_rowsplit_kernel",
+            "kernel": ROUTE_KERNELS.get(route, "?"),
             "algorithmic_bytes_per_launch": algo, "avg_launch_ms": round(fwd_mean, 4)}
     out = {
         "metric": METRIC,
@@ -246,7 +252,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{p.name}: {p.N} sequences x {p.lengths[0] if p.name != 'mixed' else 'mixed'}"
                                f" tokens, Hqk={p.Hqk}, Hv={p.Hv}, K=V=128",
-                   "token_heads": token_heads, "route": "chunk" if route == 1 else "rowsplit",
+                   "token_heads": token_heads, "route": ROUTE_NAMES.get(route, "?"),
                    "tape_interval": 256, "step": "fwd+bwd" if do_bwd else "fwd"},
         "roofline": roof,
     }

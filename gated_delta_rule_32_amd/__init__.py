@@ -33,7 +33,7 @@ SCALE = 1.0 / math.sqrt(128.0)
 KDA_OK = 0
 KDA_ERR_HIP = 12
 KDA_ERR_CAPTURE = 13
-ROUTE_AUTO, ROUTE_CHUNK, ROUTE_ROWSPLIT = 0, 1, 2
+ROUTE_AUTO, ROUTE_CHUNK, ROUTE_ROWSPLIT, ROUTE_SEGMENTS = 0, 1, 2, 3
 CONTEXT_TAPE, CONTEXT_RECORDS = 0, 1
 
 if not os.path.exists(LIB_PATH):

@@ -50,7 +50,7 @@ constexpr int kChunk = 16;
 struct Prob {
     int B, T, Hqk, Hv, N, G;
     bool packed;
-    int route;      // resolved: 1 chunk, 2 rowsplit
+    int route;      // resolved: 1 chunk, 2 rowsplit, 3 segment-parallel chunk
     int ck;         // tape interval
     int ctxmode;    // KDA_CONTEXT_TAPE or KDA_CONTEXT_RECORDS
     float scale;
@@ -61,16 +61,25 @@ struct Prob {
     int64_t total_ck;            // stored checkpoints (sum ceil(L/ck) - 1)
     int64_t total_chunks;        // sum ceil(L/16)
     int64_t total_segs;          // sum ceil(L/ck)
+    int64_t max_len;             // longest sequence
 };
 
-int auto_route(const Prob&) {
-    // The chunked MFMA kernel at all task counts.  With few tasks its one
-    // workgroup per task leaves most compute units idle, but each workgroup
-    // still advances a task about three times faster per token than the
-    // row-split kernel's sequential per-token chain spread over 8 workgroups
-    // (2 x 2048 tokens x 16 heads: 0.35 ms against 1.05 ms; 4096 tokens x 32
-    // heads x 4: 0.70 ms against 3.3 ms).  The row-split kernel stays
-    // selectable as an FP32 reference route.
+// Workgroups of the chunked kernel resident at once on MI355X (256 compute
+// units, three each).
+constexpr int64_t kChunkSlots = 768;
+
+int auto_route(const Prob& p) {
+    // The chunked MFMA kernel.  With few tasks its one workgroup per task
+    // leaves most compute units idle.  When every tape segment's P and Q run
+    // fit in one round (2 x segments x Hv <= 768) and the longest sequence
+    // has at least 4 segments, the segment-parallel form (about 2.5x the
+    // work, spread over the segments) finishes first.  The row-split kernel
+    // is slower per token than one chunked workgroup (2 x 2048 tokens x 16
+    // heads: 1.05 ms against 0.35 ms) and stays selectable as an FP32
+    // reference route.
+    if (p.ctxmode == KDA_CONTEXT_TAPE && 2 * p.total_segs * p.Hv <= kChunkSlots &&
+        p.max_len > 3 * (int64_t)p.ck)
+        return 3;
     return 1;
 }
 
@@ -93,14 +102,14 @@ kda_status validate(const kda_problem* p, Prob& out) {
         return fail(KDA_ERR_SCALE, "scale must be 1/sqrt(128) (got %g)", (double)p->scale);
     if (p->lower_bound != -5.0f)
         return fail(KDA_ERR_LOWER_BOUND, "lower_bound must be -5 (got %g)", (double)p->lower_bound);
-    if (p->route < 0 || p->route > 2) return fail(KDA_ERR_ROUTE, "unknown route %d", p->route);
+    if (p->route < 0 || p->route > 3) return fail(KDA_ERR_ROUTE, "unknown route %d", p->route);
     int ck = p->checkpoint_every == 0 ? kDefaultCk : p->checkpoint_every;
     if (ck <= 0 || ck % kChunk != 0)
         return fail(KDA_ERR_ROUTE, "checkpoint_every must be a positive multiple of 16 (got %d)",
                     p->checkpoint_every);
     if (p->context != KDA_CONTEXT_TAPE && p->context != KDA_CONTEXT_RECORDS)
         return fail(KDA_ERR_ROUTE, "unknown context kind %d", p->context);
-    if (p->context == KDA_CONTEXT_RECORDS && p->route == 2)
+    if (p->context == KDA_CONTEXT_RECORDS && (p->route == 2 || p->route == 3))
         return fail(KDA_ERR_ROUTE, "per-chunk records need the chunked route");
 
     out = Prob{};
@@ -136,8 +145,9 @@ kda_status validate(const kda_problem* p, Prob& out) {
         for (int n = 0; n < p->N; ++n) out.start[n] = (int64_t)n * p->T;
     }
     out.num_tasks = (int64_t)p->N * p->Hv;
-    out.total_ck = out.total_chunks = out.total_segs = 0;
+    out.total_ck = out.total_chunks = out.total_segs = out.max_len = 0;
     for (int64_t L : out.len) {
+        out.max_len = std::max(out.max_len, L);
         out.total_ck += (L + ck - 1) / ck - 1;
         out.total_segs += (L + ck - 1) / ck;
         out.total_chunks += (L + kChunk - 1) / kChunk;
@@ -418,9 +428,13 @@ RecLayout rec_layout(size_t recs, size_t base) {
     r.end = align256(r.ta + recs * kRecTA);
     return r;
 }
+// the segment-parallel route's P and Q of every segment, after the tape
+size_t seg_scratch_off(const Prob& p) { return align256(256 + tape_bytes(p)); }
 size_t ctx_bytes_for(const Prob& p) {
     if (p.ctxmode == KDA_CONTEXT_RECORDS)
         return rec_layout((size_t)p.total_chunks * p.Hv, 256).end;
+    if (p.route == 3)
+        return seg_scratch_off(p) + 2 * (size_t)p.total_segs * p.Hv * (size_t)kStateElems * sizeof(float);
     return 256 + tape_bytes(p);
 }
 
@@ -601,7 +615,17 @@ kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const vo
     } else if (ctx != nullptr) {
         a.tape = (float*)((char*)ctx + 256);
     }
-    e = (p.route == 1) ? kda::launch_fwd_chunk(a, stream) : kda::launch_fwd_rowsplit(a, stream);
+    if (p.route == 3 && ctx != nullptr) {
+        // segment-parallel: segment tasks; P and Q in the context after the tape
+        a.plan.task = (const int32_t*)((const char*)plan->dev + plan->off_seg);
+        a.seg_out = (float*)((char*)ctx + seg_scratch_off(p));
+        a.seg_items = p.total_segs * p.Hv;
+        e = kda::launch_fwd_segments(a, p.N, stream);
+    } else {
+        // (without a context the segment-parallel route has no tape to chain
+        // through: the plain chunked kernel runs)
+        e = (p.route != 2) ? kda::launch_fwd_chunk(a, stream) : kda::launch_fwd_rowsplit(a, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     if (ctx != nullptr) {
         CtxRecord r;

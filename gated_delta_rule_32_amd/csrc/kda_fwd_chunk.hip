@@ -130,13 +130,22 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], 
 // needs every per-token log-decay at or above -5 (so that the factors
 // exp(+-gc) stay in range); the host routes other calls elsewhere.
 // kFwdInferCkpt is the same with state checkpoints (a separate instance, so
-// that the plain one keeps its registers).
-constexpr int kFwdTape = 0, kFwdRebuild = 1, kFwdRecords = 2, kFwdInfer = 3, kFwdInferCkpt = 4;
+// that the plain one keeps its registers).  kFwdSegPQ and kFwdSegOut make the
+// segment-parallel training forward for calls with few tasks: each tape
+// segment's end state is affine in its start state, S_out = S_in P + Q, so
+// kFwdSegPQ runs every segment at once from the identity with v = 0 (giving
+// P) and from zero (giving Q), a combine kernel chains S_in through the
+// segments into the tape, and kFwdSegOut reruns every segment from its tape
+// state for o and the final state.
+constexpr int kFwdTape = 0, kFwdRebuild = 1, kFwdRecords = 2, kFwdInfer = 3, kFwdInferCkpt = 4,
+              kFwdSegPQ = 5, kFwdSegOut = 6;
 
 template <int kMode>
 __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     constexpr bool kRebuild = kMode == kFwdRebuild;  // one segment, no output
-    constexpr bool kOut = kMode != kFwdRebuild;      // o and the final state
+    constexpr bool kSegPQ = kMode == kFwdSegPQ;
+    constexpr bool kSegTask = kRebuild || kSegPQ || kMode == kFwdSegOut;  // one tape segment per task
+    constexpr bool kOut = !kRebuild && !kSegPQ;      // o and the final state
     constexpr bool kRec = kMode == kFwdRebuild || kMode == kFwdRecords;  // per-chunk records
     constexpr bool kInfer = kMode == kFwdInfer || kMode == kFwdInferCkpt;  // BF16 pool state, options
     constexpr bool kCkpt = kMode == kFwdInferCkpt;   // state checkpoints
@@ -145,10 +154,16 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     const int wave = tid >> 6;
 
     int n, h, seg = 0;
-    if constexpr (kRebuild) {
+    bool segQ = false;  // kFwdSegPQ: the second half of the grid forms Q, the first P
+    if constexpr (kSegTask) {
         // item = segment index * Hv + h; the segment list holds (n, j) pairs
-        const int sidx = blockIdx.x / a.Hv;
-        h = blockIdx.x - sidx * a.Hv;
+        int64_t item = blockIdx.x;
+        if constexpr (kSegPQ) {
+            segQ = item >= a.seg_items;
+            if (segQ) item -= a.seg_items;
+        }
+        const int sidx = (int)(item / a.Hv);
+        h = (int)(item - (int64_t)sidx * a.Hv);
         n = a.plan.task[2 * sidx];
         seg = a.plan.task[2 * sidx + 1];
     } else {
@@ -166,11 +181,11 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     int cb = 0, ce = nchunks;
     const float* src = a.s0 + slab;
     int64_t rec0 = 0;
-    if constexpr (kRebuild) {
+    if constexpr (kSegTask) {
         const int per = a.ck_every / CH;
         cb = seg * per;
         ce = min(cb + per, nchunks);
-        if (seg > 0) src = a.tape + ((tape_base + seg - 1) * a.Hv + h) * (int64_t)D * D;
+        if (!kSegPQ && seg > 0) src = a.tape + ((tape_base + seg - 1) * a.Hv + h) * (int64_t)D * D;
     }
     if constexpr (kRec) rec0 = a.plan.chunk_off[n];
     // inference: the pool slot of sequence n (checked on the host; a slot
@@ -200,6 +215,11 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 const int vcol = 16 * (2 * wave + j) + cl;
                 if constexpr (kInfer) {
                     S[kb][j] = from_bf4(*(const bf16x4*)(pinit + vcol * D + 16 * kb + 4 * gq));
+                } else if constexpr (kSegPQ) {
+                    // P: the identity (row vcol, key 16kb + 4gq + i); Q: zero
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        S[kb][j][i] = (!segQ && vcol == 16 * kb + 4 * gq + i) ? 1.0f : 0.0f;
                 } else {
                     const float4 x = *(const float4*)(src + (int64_t)vcol * D + 16 * kb + 4 * gq);
                     S[kb][j] = f32x4{x.x, x.y, x.z, x.w};
@@ -546,6 +566,12 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) id[i] = (4 * gq + i == cl) ? 1.0f : 0.0f;
             const bf16x4 ident = to_bf4(id);
+            if constexpr (kSegPQ) {
+                if (!segQ) {  // P runs with v = 0
+                    vcur.v0 = to_bf4(zero4());
+                    vcur.v1 = to_bf4(zero4());
+                }
+            }
             const bf16x4 cfv0 = to_bf4(mma16(vcur.v0, ident, zero4()));
             const bf16x4 cfv1 = to_bf4(mma16(vcur.v1, ident, zero4()));
             // a 16x16x32 costs about what a 16x16x16 does, so the hi/lo
@@ -618,7 +644,10 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 const int vcol = 16 * (2 * wave + j) + cl;
                 *(bf16x4*)(pslab + vcol * D + 16 * kb + 4 * gq) = to_bf4(S[kb][j]);
             }
-    } else if (kOut && a.s_final != nullptr) {
+    } else if constexpr (kSegPQ) {
+        const int64_t si = (segQ ? a.seg_items / a.Hv : 0) + a.plan.tape_off[n] + n + seg;
+        store_state(a.seg_out + (si * a.Hv + h) * (int64_t)D * D, S, wave, (tid & 63) >> 4, tid & 15);
+    } else if (kOut && a.s_final != nullptr && ce == nchunks) {
         store_state(a.s_final + slab, S, wave, (tid & 63) >> 4, tid & 15);
     }
 }
@@ -644,6 +673,81 @@ hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s) {
 hipError_t launch_state_rebuild(const FwdArgs& a, int64_t num_items, hipStream_t s) {
     if (num_items == 0) return hipSuccess;
     hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRebuild>, dim3((unsigned)num_items), dim3(FC_THREADS), 0, s, a);
+    return hipGetLastError();
+}
+
+// Chains the start states through the segments of every (sequence, value
+// head): S_in(j) = S_in(j-1) P(j-1) + Q(j-1), written to tape row j-1.  Value
+// rows are independent, so each workgroup takes 16 rows of one task (8 per
+// task) and keeps them in LDS; wave w forms output columns 32w..32w+31 with
+// FP32 16x16x4 MFMAs (FP32 products and sums), P read from L2.
+__global__ __launch_bounds__(256) void seg_combine_kernel(FwdArgs a) {
+    constexpr int SP = D + 1;  // padded row: the 16 rows of a K-step sit in distinct banks
+    __shared__ float sr[16 * SP];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
+    const int rb = blockIdx.x & 7;
+    const int nh = blockIdx.x >> 3;
+    const int n = nh / a.Hv, h = nh - n * a.Hv;
+    const int L = a.plan.seq_len[n];
+    const int nseg = (L + a.ck_every - 1) / a.ck_every;
+    if (nseg < 2) return;  // uniform over the workgroup: before any barrier
+    const int64_t toff = a.plan.tape_off[n];
+    const int64_t DD = (int64_t)D * D;
+    const int64_t segs = a.seg_items / a.Hv;
+    {
+        const float* s0 = a.s0 + ((int64_t)n * a.Hv + h) * DD + (int64_t)(16 * rb) * D;
+        for (int e = tid; e < 16 * D; e += 256) sr[(e / D) * SP + (e % D)] = s0[e];
+    }
+    for (int j = 1; j < nseg; ++j) {
+        const int64_t sj = toff + n + (j - 1);  // segment j-1 of sequence n
+        const float* P = a.seg_out + (sj * a.Hv + h) * DD;
+        const float* Q = a.seg_out + ((segs + sj) * a.Hv + h) * DD;
+        __syncthreads();  // rows of S_in(j-1) in LDS
+        f32x4 acc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col = 16 * (2 * wave + t) + cl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] = Q[(int64_t)(16 * rb + 4 * gq + i) * D + col];
+        }
+#pragma unroll 8
+        for (int kk = 0; kk < D; kk += 4) {
+            const float x = sr[cl * SP + kk + gq];  // A[row cl][k = kk + gq]
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const float y = P[(int64_t)(kk + gq) * D + 16 * (2 * wave + t) + cl];  // B[k][col]
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc[t], 0, 0, 0);
+            }
+        }
+        __syncthreads();  // every wave has read S_in(j-1)
+        float* dst = a.tape + ((toff + j - 1) * a.Hv + h) * DD + (int64_t)(16 * rb) * D;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col = 16 * (2 * wave + t) + cl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {  // lane (gq, cl) holds rows 4gq+i, column col
+                sr[(4 * gq + i) * SP + col] = acc[t][i];
+                dst[(4 * gq + i) * D + col] = acc[t][i];
+            }
+        }
+    }
+}
+
+// The segment-parallel forward (needs a.tape, a.seg_out and a.seg_items):
+// P and Q of every segment, the chain through the tape, then every segment
+// again for o and the final state.  The plan's task list must be the segment
+// list; N is the number of sequences.
+hipError_t launch_fwd_segments(const FwdArgs& a, int N, hipStream_t s) {
+    if (a.seg_items == 0) return hipSuccess;
+    hipLaunchKernelGGL(fwd_chunk_kernel<kFwdSegPQ>, dim3((unsigned)(2 * a.seg_items)), dim3(FC_THREADS), 0,
+                       s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(N * a.Hv * 8)), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fwd_chunk_kernel<kFwdSegOut>, dim3((unsigned)a.seg_items), dim3(FC_THREADS), 0, s, a);
     return hipGetLastError();
 }
 

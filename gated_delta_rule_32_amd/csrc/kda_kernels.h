@@ -59,6 +59,11 @@ struct FwdArgs {
     bf16_t* ckpt;           // null: none
     const int64_t* ckpt_start;
     int64_t ckpt_rows;      // rows of ckpt; a row outside [0, ckpt_rows) is not stored
+    // Segment-parallel forward: seg_out is [2][segments][Hv][128][128] FP32,
+    // the transfer P and offset Q of every tape segment (segment index
+    // tape_off[n] + n + j), and seg_items = segments * Hv.
+    float* seg_out;
+    int64_t seg_items;
     int ckpt_every;
     // speculative decode (spec_tokens = S > 0): pool_index is [N][1+S]; the
     // state is read from slot [n][a-1] (a = spec_accepted[n] clamped to
@@ -87,6 +92,7 @@ hipError_t launch_fwd_rowsplit(const FwdArgs& a, hipStream_t s);
 hipError_t launch_infer_token(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s);
 hipError_t launch_state_rebuild(const FwdArgs& a, int64_t num_items, hipStream_t s);
+hipError_t launch_fwd_segments(const FwdArgs& a, int N, hipStream_t s);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdArgs& a, int N, hipStream_t s);
 

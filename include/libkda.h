@@ -96,9 +96,18 @@ typedef enum {
 } kda_status;
 
 typedef enum {
-    KDA_ROUTE_AUTO = 0,      /* library chooses (currently always the chunked kernel) */
+    KDA_ROUTE_AUTO = 0,      /* library chooses (see kda_plan_query) */
     KDA_ROUTE_CHUNK = 1,     /* chunked MFMA kernel */
-    KDA_ROUTE_ROWSPLIT = 2   /* per-token FP32 kernel, state rows split across workgroups */
+    KDA_ROUTE_ROWSPLIT = 2,  /* per-token FP32 kernel, state rows split across workgroups */
+    KDA_ROUTE_SEGMENTS = 3   /* training forward with the tape context only: the chunked
+                                kernel over all tape segments at once.  Each segment's
+                                end state is affine in its start state (S_in P + Q); P
+                                and Q of every segment are formed in parallel, chained
+                                into the tape, and every segment is rerun for o.  The
+                                context is larger by 2 states per segment and head.
+                                AUTO takes it when 2 x segments x Hv <= 768 and the
+                                longest sequence spans 4 or more tape segments.  Without
+                                a context the plain chunked kernel runs. */
 } kda_route;
 
 /* What the training forward saves for the backward.  TAPE: the FP32 state

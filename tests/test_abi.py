@@ -84,8 +84,18 @@ def test_context_and_workspace_sizes():
     # 300 -> 1, 1 -> 0, 511 -> 1
     assert kda.kda_fwd_ctx_bytes(p) == 256 + 2 * 2 * 128 * 128 * 4
     p.checkpoint_every = 64
+    p.route = kda.ROUTE_CHUNK
     n_ck = (300 + 63) // 64 - 1 + 0 + (511 + 63) // 64 - 1
-    assert kda.kda_fwd_ctx_bytes(p) == 256 + n_ck * 2 * 128 * 128 * 4
+    tape = n_ck * 2 * 128 * 128 * 4
+    assert kda.kda_fwd_ctx_bytes(p) == 256 + tape
+    # with 5 + 1 + 8 segments (2 x 14 x 2 <= 768) and the longest sequence
+    # spanning 8 of them, AUTO takes the segment-parallel route, whose context
+    # adds P and Q of every segment after the tape (256-byte aligned)
+    p.route = kda.ROUTE_AUTO
+    assert kda.kda_plan_query(p)[0] == kda.ROUTE_SEGMENTS
+    segs = 5 + 1 + 8
+    assert kda.kda_fwd_ctx_bytes(p) == (256 + tape + 255) // 256 * 256 + 2 * segs * 2 * 128 * 128 * 4
+    p.route = kda.ROUTE_CHUNK
     chunks = sum((L + 15) // 16 for L in (300, 1, 511))
     ws = kda.kda_bwd_workspace_bytes(p)
     # per (chunk, value head): BF16 chunk-start state, BF16 U, FP32 T/Akk/Aqk;

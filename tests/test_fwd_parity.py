@@ -79,6 +79,38 @@ def test_forward_deterministic(route):
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
 
 
+def _segment_cases():
+    P = workloads.Problem
+    return {  # (problem, seed, tape interval): several segments per sequence, tails, one-segment sequences
+        "ragged_ck32": (P([1, 15, 16, 17, 33, 100, 250], 2, 4, packed=True), 110, 32),
+        "fixed_ck64": (P([300] * 2, 1, 2, packed=False), 111, 64),
+        "grouped_ck16": (P([40, 70], 2, 8, packed=True), 112, 16),
+    }
+
+
+@pytest.mark.parametrize("case", list(_segment_cases().keys()))
+def test_forward_segments(case):
+    """The segment-parallel route: o and the final state against the oracle,
+    and its tape (states chained through the segments as S_in P + Q) against
+    the plain chunked route's tape, at the FP32 state bar."""
+    problem, seed, ck = _segment_cases()[case]
+    inp = workloads.make_inputs(problem, seed, with_adjoints=False)
+    print(f"[fwd] segments case={case} ck={ck} lengths={problem.lengths[:8]}", flush=True)
+    o, fs, ctx, _ = pu.run_forward(inp, route=3, ckpt=ck, save_context=True)
+    ref_o, ref_s = pu.oracle_forward(inp)
+    pu.assert_close("o", o.float().cpu().numpy(), ref_o)
+    pu.assert_state_close("final_state", fs.cpu().numpy(), ref_s)
+    o1, f1, ctx1, _ = pu.run_forward(inp, route=1, ckpt=ck, save_context=True)
+    n_ck = sum(-(-L // ck) - 1 for L in problem.lengths)
+    tape_bytes = n_ck * problem.Hv * 128 * 128 * 4
+    t3 = ctx.ctx[256:256 + tape_bytes].view(torch.float32).cpu().numpy()
+    t1 = ctx1.ctx[256:256 + tape_bytes].view(torch.float32).cpu().numpy()
+    assert np.isfinite(t3).all()
+    assert np.abs(t3 - t1).max() < pu.STATE_ATOL
+    assert (o.float() - o1.float()).abs().max().item() < 2e-3
+    assert (fs - f1).abs().max().item() < pu.STATE_ATOL
+
+
 def test_routes_agree():
     """Both routes compute the same recurrence: their outputs agree to well
     inside the tolerance."""
