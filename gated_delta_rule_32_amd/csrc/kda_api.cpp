@@ -530,7 +530,7 @@ kda_status kda_fwd_ctx_bytes(const kda_problem* pp, size_t* bytes) {
 // state, BF16 U, FP32 T^T / Akk^T / Aqk), then FP32 dq/dk partials when value
 // heads share a q/k head, then per-task parameter-gradient partials.
 struct WsLayout {
-    size_t s0, u, ta, dqk, par, total;
+    size_t s0, u, ta, dqk, par, seg_r, seg_e, total;
 };
 static WsLayout ws_layout(const Prob& p) {
     WsLayout w;
@@ -544,7 +544,15 @@ static WsLayout ws_layout(const Prob& p) {
     w.dqk = off;
     if (p.G > 1) off = align256(off + (size_t)p.tokens * p.Hv * 2 * D * sizeof(float));
     w.par = off;
-    off = align256(off + (size_t)p.num_tasks * 2 * D * sizeof(float));
+    // parameter partials per task, or per (segment, head) on the segment-parallel route
+    const bool segs = p.route == 3 && p.ctxmode == KDA_CONTEXT_TAPE;
+    const size_t slots = segs ? (size_t)std::max<int64_t>(p.num_tasks, p.total_segs * p.Hv) : (size_t)p.num_tasks;
+    off = align256(off + slots * 2 * D * sizeof(float));
+    // segment-parallel adjoint: R and the chained segment-end dS per (segment, head)
+    w.seg_r = off;
+    if (segs) off = align256(off + (size_t)p.total_segs * p.Hv * kStateElems * sizeof(float));
+    w.seg_e = off;
+    if (segs) off = align256(off + (size_t)p.total_segs * p.Hv * kStateElems * sizeof(float));
     w.total = off;
     return w;
 }
@@ -738,9 +746,22 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
         e = kda::launch_state_rebuild(rb, p.total_segs * p.Hv, stream);
         if (e != hipSuccess) return hip_fail(e, "state rebuild launch");
     }
-    e = kda::launch_bwd_chunk(b, stream);
+    int partial_rows = p.N;
+    if (p.route == 3 && !records) {
+        // segment-parallel adjoint over the tape segments, with the forward's P
+        kda::BwdArgs bs = b;
+        bs.f.plan.task = (const int32_t*)((const char*)plan->dev + plan->off_seg);
+        bs.f.seg_items = p.total_segs * p.Hv;
+        bs.seg_p = (const float*)((const char*)ctx + seg_scratch_off(p));
+        bs.seg_r = (float*)(ws + wl.seg_r);
+        bs.seg_e = (float*)(ws + wl.seg_e);
+        e = kda::launch_bwd_segments(bs, p.N, stream);
+        partial_rows = (int)p.total_segs;  // partials per (segment, head)
+    } else {
+        e = kda::launch_bwd_chunk(b, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "backward launch");
-    e = kda::launch_bwd_reduce(b, p.N, stream);
+    e = kda::launch_bwd_reduce(b, partial_rows, stream);
     if (e != hipSuccess) return hip_fail(e, "backward reduction launch");
     return KDA_OK;
 }

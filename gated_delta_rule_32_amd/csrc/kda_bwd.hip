@@ -121,9 +121,20 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
 
-    const int code = a.plan.task[blockIdx.x];
-    const int n = code / a.Hv;
-    const int h = code - n * a.Hv;
+    int n, h, seg = 0, code;
+    int64_t segidx = 0;
+    if (b.seg_pass != 0) {  // item = segment list index * Hv + h
+        const int sidx = blockIdx.x / a.Hv;
+        h = blockIdx.x - sidx * a.Hv;
+        n = a.plan.task[2 * sidx];
+        seg = a.plan.task[2 * sidx + 1];
+        segidx = a.plan.tape_off[n] + n + seg;
+        code = (int)segidx * a.Hv + h;  // parameter-partial slot
+    } else {
+        code = a.plan.task[blockIdx.x];
+        n = code / a.Hv;
+        h = code - n * a.Hv;
+    }
     const int hq = h / a.G;
     const int64_t tok0 = a.plan.seq_start[n];
     const int L = a.plan.seq_len[n];
@@ -131,6 +142,13 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     const int64_t rec0 = a.plan.chunk_off[n];
     const int nchunks = (L + CH - 1) / CH;
     const int nfull = L / CH;
+    // chunks [cb, ce): the whole task, or one tape segment
+    int cb = 0, ce = nchunks;
+    if (b.seg_pass != 0) {
+        cb = seg * (a.ck_every / CH);
+        ce = min(cb + a.ck_every / CH, nchunks);
+    }
+    const bool last_seg = ce == nchunks;
     const float eA = __expf(a.A_log[h]);
     const float zs = eA * LOG2E;
     const float scale = a.scale;
@@ -161,7 +179,11 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     };
 
     // dS frags: dS[vb][j] for kb = 2*wave + j, lane (gq, k) holds
-    // dS[16vb + 4gq + i][16kb + k]; starts at dfinal_state
+    // dS[16vb + 4gq + i][16kb + k]; starts at dfinal_state (the last segment),
+    // zero (pass 1) or the chained segment end (pass 2)
+    const float* ds_src = b.dfinal + slab;
+    if (b.seg_pass == 2 && !last_seg) ds_src = b.seg_e + (segidx * a.Hv + h) * (int64_t)D * D;
+    const bool ds_zero = b.seg_pass == 1;
     f32x4 dS[8][2];
     {
         // addresses from an opaque copy of the thread id: the epilogue's
@@ -176,7 +198,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    dS[vb][j][i] = b.dfinal[slab + (int64_t)(16 * vb + 4 * gq + i) * D + 16 * (2 * wave + j) + cl];
+                    dS[vb][j][i] = ds_zero ? 0.f : ds_src[(int64_t)(16 * vb + 4 * gq + i) * D + 16 * (2 * wave + j) + cl];
     }
     if (tid < D) sm.dtz[tid] = a.dt_bias[h * D + tid] * zs;
     float ddt_acc[2][4];
@@ -187,7 +209,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     float dA_acc = 0.f;
 
     RowIn cur;
-    load_row(cur, min((nchunks - 1) * CH + (tid >> 4), L - 1), (tid & 15) * 8);
+    load_row(cur, min((ce - 1) * CH + (tid >> 4), L - 1), (tid & 15) * 8);
     __syncthreads();
     // ---- P1 of chunk ci: norms, gate, beta (row-owner mapping) from the
     // rows in `cur`.  Run for chunk ci-1 in chunk ci's last phase (it writes
@@ -226,7 +248,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             }
         }
     };
-    p1(nchunks - 1);
+    p1(ce - 1);
     __syncthreads();
 
     auto chunk = [&](const int ci, auto tail_tag) __attribute__((always_inline)) {
@@ -671,11 +693,11 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 *at(dbetap, __umul24(tc, sb)) = (bf16)(db * bt * (1.0f - bt));
             }
         }
-        if (ci > 0) p1(ci - 1);
+        if (ci > cb) p1(ci - 1);
         __syncthreads();
     };
-    if (nfull < nchunks) chunk(nfull, std::true_type{});
-    for (int ci = nfull - 1; ci >= 0; --ci) chunk(ci, std::false_type{});
+    if (last_seg && nfull < nchunks) chunk(nfull, std::true_type{});
+    for (int ci = min(nfull, ce) - 1; ci >= cb; --ci) chunk(ci, std::false_type{});
 
     // dinitial_state, parameter partials
     {
@@ -687,8 +709,14 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    b.dinit[slab + (int64_t)(16 * vb + 4 * gq + i) * D + 16 * (2 * wave + j) + cl] = dS[vb][j][i];
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t e = (int64_t)(16 * vb + 4 * gq + i) * D + 16 * (2 * wave + j) + cl;
+                    if (b.seg_pass == 1)  // R: the segment's start dS from zero
+                        b.seg_r[(segidx * a.Hv + h) * (int64_t)D * D + e] = dS[vb][j][i];
+                    else if (cb == 0)
+                        b.dinit[slab + e] = dS[vb][j][i];
+                }
+        if (b.seg_pass == 1) return;  // no parameter partials from pass 1
         float* pp = b.dparam_part + (int64_t)code * 2 * D;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -740,6 +768,81 @@ __global__ void bwd_dqk_reduce_kernel(BwdArgs b, int64_t items) {
 hipError_t launch_bwd_chunk(const BwdArgs& b, hipStream_t s) {
     if (b.f.num_tasks == 0) return hipSuccess;
     hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)b.f.num_tasks), dim3(BW_THREADS), 0, s, b);
+    return hipGetLastError();
+}
+
+// dS_end(j-1) = dS_end(j) P(j)^T + R(j), from dfinal at the last segment, for
+// 16 value rows of one task per workgroup (value rows are independent): the
+// forward's combine run backward with P transposed.
+__global__ __launch_bounds__(256) void seg_combine_bwd_kernel(BwdArgs b) {
+    const FwdArgs& a = b.f;
+    constexpr int SP = D + 1;
+    __shared__ float sr[16 * SP];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, gq = lane >> 4, cl = lane & 15;
+    const int rb = blockIdx.x & 7;
+    const int nh = blockIdx.x >> 3;
+    const int n = nh / a.Hv, h = nh - n * a.Hv;
+    const int L = a.plan.seq_len[n];
+    const int nseg = (L + a.ck_every - 1) / a.ck_every;
+    if (nseg < 2) return;  // uniform over the workgroup: before any barrier
+    const int64_t base = a.plan.tape_off[n] + n;  // segment index of segment 0
+    const int64_t DD = (int64_t)D * D;
+    {
+        const float* df = b.dfinal + ((int64_t)n * a.Hv + h) * DD + (int64_t)(16 * rb) * D;
+        for (int e = tid; e < 16 * D; e += 256) sr[(e / D) * SP + (e % D)] = df[e];
+    }
+    for (int j = nseg - 1; j >= 1; --j) {
+        const float* P = b.seg_p + ((base + j) * a.Hv + h) * DD;
+        const float* R = b.seg_r + ((base + j) * a.Hv + h) * DD;
+        __syncthreads();  // rows of dS_end(j) in LDS
+        f32x4 acc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col = 16 * (2 * wave + t) + cl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] = R[(int64_t)(16 * rb + 4 * gq + i) * D + col];
+        }
+#pragma unroll 8
+        for (int kk = 0; kk < D; kk += 4) {
+            const float x = sr[cl * SP + kk + gq];  // A[row cl][k = kk + gq]
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                // B[k][col] = P^T[k][col] = P[col][k]
+                const float y = P[(int64_t)(16 * (2 * wave + t) + cl) * D + kk + gq];
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc[t], 0, 0, 0);
+            }
+        }
+        __syncthreads();  // every wave has read dS_end(j)
+        float* dst = b.seg_e + ((base + j - 1) * a.Hv + h) * DD + (int64_t)(16 * rb) * D;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int col = 16 * (2 * wave + t) + cl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sr[(4 * gq + i) * SP + col] = acc[t][i];
+                dst[(4 * gq + i) * D + col] = acc[t][i];
+            }
+        }
+    }
+}
+
+// The segment-parallel adjoint (after the state rebuild): pass 1 over every
+// segment, the chain, pass 2 over every segment.  b.f.plan.task must be the
+// segment list and b.f.seg_items its length times Hv.
+hipError_t launch_bwd_segments(const BwdArgs& b, int N, hipStream_t s) {
+    if (b.f.seg_items == 0) return hipSuccess;
+    BwdArgs p1 = b;
+    p1.seg_pass = 1;
+    hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)b.f.seg_items), dim3(BW_THREADS), 0, s, p1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(seg_combine_bwd_kernel, dim3((unsigned)(N * b.f.Hv * 8)), dim3(256), 0, s, b);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    BwdArgs p2 = b;
+    p2.seg_pass = 2;
+    hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)b.f.seg_items), dim3(BW_THREADS), 0, s, p2);
     return hipGetLastError();
 }
 

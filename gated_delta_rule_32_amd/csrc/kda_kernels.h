@@ -86,6 +86,17 @@ struct BwdArgs {
     float* dqk_part;        // [tokens][Hv][2][128] FP32 partial dq,dk when G > 1; else null
     float* dparam_part;     // [tasks][2][128]: per-task ddt_bias and dA_log partial sums
     int64_t total_tokens;
+    // Segment-parallel adjoint (seg_pass 1 or 2; 0: whole tasks).  Tasks are
+    // tape segments (f.plan.task is the segment list, f.seg_items = segments
+    // * Hv; segment index tape_off[n] + n + j).  Pass 1 runs each segment
+    // from dS = 0 and stores its start dS to seg_r; a combine chains
+    // dS_end(j-1) = dS_end(j) P(j)^T + R(j) into seg_e; pass 2 runs each
+    // segment from dfinal (last segment) or seg_e for the gradients, with
+    // the parameter partials per segment.  seg_p is the forward's P.
+    int seg_pass;
+    const float* seg_p;
+    float* seg_r;
+    float* seg_e;
 };
 
 hipError_t launch_fwd_rowsplit(const FwdArgs& a, hipStream_t s);
@@ -95,5 +106,6 @@ hipError_t launch_state_rebuild(const FwdArgs& a, int64_t num_items, hipStream_t
 hipError_t launch_fwd_segments(const FwdArgs& a, int N, hipStream_t s);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdArgs& a, int N, hipStream_t s);
+hipError_t launch_bwd_segments(const BwdArgs& a, int N, hipStream_t s);
 
 }  // namespace kda
