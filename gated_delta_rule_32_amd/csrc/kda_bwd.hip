@@ -115,6 +115,9 @@ __device__ __forceinline__ f32x4 mma16_split(bf16x4 ah, bf16x4 al, bf16x4 bh, bf
 
 }  // namespace
 
+// kSeg: the segment-parallel passes (b.seg_pass 1 or 2), a separate instance
+// so that the whole-task one keeps its code.
+template <bool kSeg>
 __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     __shared__ BwdLds sm;
     const FwdArgs& a = b.f;
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
 
     int n, h, seg = 0, code;
     int64_t segidx = 0;
-    if (b.seg_pass != 0) {  // item = segment list index * Hv + h
+    if constexpr (kSeg) {  // item = segment list index * Hv + h
         const int sidx = blockIdx.x / a.Hv;
         h = blockIdx.x - sidx * a.Hv;
         n = a.plan.task[2 * sidx];
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     const int nfull = L / CH;
     // chunks [cb, ce): the whole task, or one tape segment
     int cb = 0, ce = nchunks;
-    if (b.seg_pass != 0) {
+    if constexpr (kSeg) {
         cb = seg * (a.ck_every / CH);
         ce = min(cb + a.ck_every / CH, nchunks);
     }
@@ -182,8 +185,11 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     // dS[16vb + 4gq + i][16kb + k]; starts at dfinal_state (the last segment),
     // zero (pass 1) or the chained segment end (pass 2)
     const float* ds_src = b.dfinal + slab;
-    if (b.seg_pass == 2 && !last_seg) ds_src = b.seg_e + (segidx * a.Hv + h) * (int64_t)D * D;
-    const bool ds_zero = b.seg_pass == 1;
+    bool ds_zero = false;
+    if constexpr (kSeg) {
+        if (b.seg_pass == 2 && !last_seg) ds_src = b.seg_e + (segidx * a.Hv + h) * (int64_t)D * D;
+        ds_zero = b.seg_pass == 1;
+    }
     f32x4 dS[8][2];
     {
         // addresses from an opaque copy of the thread id: the epilogue's
@@ -711,12 +717,12 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int64_t e = (int64_t)(16 * vb + 4 * gq + i) * D + 16 * (2 * wave + j) + cl;
-                    if (b.seg_pass == 1)  // R: the segment's start dS from zero
+                    if (kSeg && b.seg_pass == 1)  // R: the segment's start dS from zero
                         b.seg_r[(segidx * a.Hv + h) * (int64_t)D * D + e] = dS[vb][j][i];
                     else if (cb == 0)
                         b.dinit[slab + e] = dS[vb][j][i];
                 }
-        if (b.seg_pass == 1) return;  // no parameter partials from pass 1
+        if (kSeg && b.seg_pass == 1) return;  // no parameter partials from pass 1
         float* pp = b.dparam_part + (int64_t)code * 2 * D;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -767,7 +773,7 @@ __global__ void bwd_dqk_reduce_kernel(BwdArgs b, int64_t items) {
 
 hipError_t launch_bwd_chunk(const BwdArgs& b, hipStream_t s) {
     if (b.f.num_tasks == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)b.f.num_tasks), dim3(BW_THREADS), 0, s, b);
+    hipLaunchKernelGGL(bwd_chunk_kernel<false>, dim3((unsigned)b.f.num_tasks), dim3(BW_THREADS), 0, s, b);
     return hipGetLastError();
 }
 
@@ -834,7 +840,7 @@ hipError_t launch_bwd_segments(const BwdArgs& b, int N, hipStream_t s) {
     if (b.f.seg_items == 0) return hipSuccess;
     BwdArgs p1 = b;
     p1.seg_pass = 1;
-    hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)b.f.seg_items), dim3(BW_THREADS), 0, s, p1);
+    hipLaunchKernelGGL(bwd_chunk_kernel<true>, dim3((unsigned)b.f.seg_items), dim3(BW_THREADS), 0, s, p1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(seg_combine_bwd_kernel, dim3((unsigned)(N * b.f.Hv * 8)), dim3(256), 0, s, b);
@@ -842,7 +848,7 @@ hipError_t launch_bwd_segments(const BwdArgs& b, int N, hipStream_t s) {
     if (e != hipSuccess) return e;
     BwdArgs p2 = b;
     p2.seg_pass = 2;
-    hipLaunchKernelGGL(bwd_chunk_kernel, dim3((unsigned)b.f.seg_items), dim3(BW_THREADS), 0, s, p2);
+    hipLaunchKernelGGL(bwd_chunk_kernel<true>, dim3((unsigned)b.f.seg_items), dim3(BW_THREADS), 0, s, p2);
     return hipGetLastError();
 }
 
