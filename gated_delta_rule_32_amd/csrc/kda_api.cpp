@@ -428,13 +428,13 @@ RecLayout rec_layout(size_t recs, size_t base) {
     r.end = align256(r.ta + recs * kRecTA);
     return r;
 }
-// the segment-parallel route's P and Q of every segment, after the tape
+// the segment-parallel route's P, Q and P^T of every segment, after the tape
 size_t seg_scratch_off(const Prob& p) { return align256(256 + tape_bytes(p)); }
 size_t ctx_bytes_for(const Prob& p) {
     if (p.ctxmode == KDA_CONTEXT_RECORDS)
         return rec_layout((size_t)p.total_chunks * p.Hv, 256).end;
     if (p.route == 3)
-        return seg_scratch_off(p) + 2 * (size_t)p.total_segs * p.Hv * (size_t)kStateElems * sizeof(float);
+        return seg_scratch_off(p) + 3 * (size_t)p.total_segs * p.Hv * (size_t)kStateElems * sizeof(float);
     return 256 + tape_bytes(p);
 }
 
@@ -752,7 +752,8 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
         kda::BwdArgs bs = b;
         bs.f.plan.task = (const int32_t*)((const char*)plan->dev + plan->off_seg);
         bs.f.seg_items = p.total_segs * p.Hv;
-        bs.seg_p = (const float*)((const char*)ctx + seg_scratch_off(p));
+        bs.seg_p = (const float*)((const char*)ctx + seg_scratch_off(p) +
+                                  2 * (size_t)p.total_segs * p.Hv * kStateElems * sizeof(float));  // P^T
         bs.seg_r = (float*)(ws + wl.seg_r);
         bs.seg_e = (float*)(ws + wl.seg_e);
         e = kda::launch_bwd_segments(bs, p.N, stream);

@@ -814,8 +814,8 @@ __global__ __launch_bounds__(256) void seg_combine_bwd_kernel(BwdArgs b) {
             const float x = sr[cl * SP + kk + gq];  // A[row cl][k = kk + gq]
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                // B[k][col] = P^T[k][col] = P[col][k]
-                const float y = P[(int64_t)(16 * (2 * wave + t) + cl) * D + kk + gq];
+                // B[k][col] = P^T[k][col], stored row-major
+                const float y = P[(int64_t)(kk + gq) * D + 16 * (2 * wave + t) + cl];
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc[t], 0, 0, 0);
             }
         }

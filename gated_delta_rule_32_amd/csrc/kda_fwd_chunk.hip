@@ -645,8 +645,24 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 *(bf16x4*)(pslab + vcol * D + 16 * kb + 4 * gq) = to_bf4(S[kb][j]);
             }
     } else if constexpr (kSegPQ) {
-        const int64_t si = (segQ ? a.seg_items / a.Hv : 0) + a.plan.tape_off[n] + n + seg;
+        const int64_t segs = a.seg_items / a.Hv;
+        const int64_t sj = a.plan.tape_off[n] + n + seg;
+        const int64_t si = (segQ ? segs : 0) + sj;
         store_state(a.seg_out + (si * a.Hv + h) * (int64_t)D * D, S, wave, (tid & 63) >> 4, tid & 15);
+        if (!segQ) {
+            // P transposed as well (third slab), for the adjoint's chain:
+            // lane (gq, cl) holds P[vcol][16kb + 4gq + i]; adjacent lanes
+            // write adjacent columns of row 16kb + 4gq + i
+            float* pt = a.seg_out + ((2 * segs + sj) * a.Hv + h) * (int64_t)D * D;
+            const int lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        pt[(16 * kb + 4 * gq + i) * D + 16 * (2 * wave + j) + cl] = S[kb][j][i];
+        }
     } else if (kOut && a.s_final != nullptr && ce == nchunks) {
         store_state(a.s_final + slab, S, wave, (tid & 63) >> 4, tid & 15);
     }

@@ -59,9 +59,9 @@ struct FwdArgs {
     bf16_t* ckpt;           // null: none
     const int64_t* ckpt_start;
     int64_t ckpt_rows;      // rows of ckpt; a row outside [0, ckpt_rows) is not stored
-    // Segment-parallel forward: seg_out is [2][segments][Hv][128][128] FP32,
-    // the transfer P and offset Q of every tape segment (segment index
-    // tape_off[n] + n + j), and seg_items = segments * Hv.
+    // Segment-parallel forward: seg_out is [3][segments][Hv][128][128] FP32,
+    // the transfer P, offset Q and P transposed of every tape segment
+    // (segment index tape_off[n] + n + j), and seg_items = segments * Hv.
     float* seg_out;
     int64_t seg_items;
     int ckpt_every;
@@ -92,7 +92,8 @@ struct BwdArgs {
     // from dS = 0 and stores its start dS to seg_r; a combine chains
     // dS_end(j-1) = dS_end(j) P(j)^T + R(j) into seg_e; pass 2 runs each
     // segment from dfinal (last segment) or seg_e for the gradients, with
-    // the parameter partials per segment.  seg_p is the forward's P.
+    // the parameter partials per segment.  seg_p is the forward's P
+    // transposed (row-major P^T).
     int seg_pass;
     const float* seg_p;
     float* seg_r;

@@ -104,7 +104,9 @@ typedef enum {
                                 end state is affine in its start state (S_in P + Q); P
                                 and Q of every segment are formed in parallel, chained
                                 into the tape, and every segment is rerun for o.  The
-                                context is larger by 2 states per segment and head.
+                                context is larger by 3 states per segment and head
+                                (P, Q and P transposed, which the backward chains
+                                with).
                                 AUTO takes it when 2 x segments x Hv <= 768 and the
                                 longest sequence spans 4 or more tape segments.  Without
                                 a context the plain chunked kernel runs. */

@@ -90,11 +90,11 @@ def test_context_and_workspace_sizes():
     assert kda.kda_fwd_ctx_bytes(p) == 256 + tape
     # with 5 + 1 + 8 segments (2 x 14 x 2 <= 768) and the longest sequence
     # spanning 8 of them, AUTO takes the segment-parallel route, whose context
-    # adds P and Q of every segment after the tape (256-byte aligned)
+    # adds P, Q and P transposed of every segment after the tape (256-byte aligned)
     p.route = kda.ROUTE_AUTO
     assert kda.kda_plan_query(p)[0] == kda.ROUTE_SEGMENTS
     segs = 5 + 1 + 8
-    assert kda.kda_fwd_ctx_bytes(p) == (256 + tape + 255) // 256 * 256 + 2 * segs * 2 * 128 * 128 * 4
+    assert kda.kda_fwd_ctx_bytes(p) == (256 + tape + 255) // 256 * 256 + 3 * segs * 2 * 128 * 128 * 4
     p.route = kda.ROUTE_CHUNK
     chunks = sum((L + 15) // 16 for L in (300, 1, 511))
     ws = kda.kda_bwd_workspace_bytes(p)
