@@ -13,10 +13,13 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 P = workloads.Problem
-CASES = {
-    "ragged_tape": (P([1, 15, 16, 17, 33, 100, 300], 2, 4, packed=True), 400, 0),
-    "ragged_records": (P([5, 64, 250], 1, 2, packed=True), 401, 1),
-    "fixed_tape": (P([96] * 2, 2, 2, packed=False), 402, 0),
+CASES = {  # (problem, seed, context kind, route, tape interval)
+    "ragged_tape": (P([1, 15, 16, 17, 33, 100, 300], 2, 4, packed=True), 400, 0, 1, 0),
+    "ragged_records": (P([5, 64, 250], 1, 2, packed=True), 401, 1, 1, 0),
+    "fixed_tape": (P([96] * 2, 2, 2, packed=False), 402, 0, 1, 0),
+    # the segment-parallel route: P/Q, chain and rerun launches, and the
+    # segmented adjoint's two passes and reverse chain
+    "segments_tape": (P([300, 47, 200], 1, 2, packed=True), 403, 0, 3, 64),
 }
 
 
@@ -24,13 +27,13 @@ class _Step:
     """Static buffers for one forward + backward, so that the captured
     launches keep valid pointers."""
 
-    def __init__(self, inp, context):
+    def __init__(self, inp, context, route=1, ckpt=0):
         import gated_delta_rule_32_amd as kda
         self.kda = kda
         self.d = d = inp.to("cuda")
         p = inp.problem
         self.prob = kda.make_problem(p.B, p.T, p.Hqk, p.Hv, p.N, d.cu_seqlens, inp.cu_seqlens,
-                                     route=1, context=context)
+                                     route=route, checkpoint_every=ckpt, context=context)
         self.o = torch.empty_like(d.v)
         self.fs = torch.empty_like(d.initial_state)
         self.ctx = torch.empty(kda.kda_fwd_ctx_bytes(self.prob), dtype=torch.uint8, device="cuda")
@@ -56,10 +59,10 @@ def _host(ts):
 
 @pytest.mark.parametrize("case", list(CASES.keys()))
 def test_captured_step_replays_match_eager(case):
-    problem, seed, context = CASES[case]
+    problem, seed, context, route, ckpt = CASES[case]
     inp = workloads.make_inputs(problem, seed, with_adjoints=True)
     print(f"[graph] case={case} lengths={problem.lengths}", flush=True)
-    step = _Step(inp, context)
+    step = _Step(inp, context, route, ckpt)
     # two eager calls: the first makes and uploads the schedule, the second
     # (after the device finished) observes the upload as complete
     step.run()
