@@ -99,6 +99,37 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     print(json.dumps({"copy_calibration_bytes_per_copy": nbytes, "copies": reps}), flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_bandwidth(stream, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """GB/s (bytes read plus bytes written) of a plain 1 GiB device copy,
+    timed with HIP events on `stream`: the practical HBM ceiling of this GPU
+    in this job, next to the nominal 8 TB/s."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(inp, max_seconds: float = 30.0):
     import numpy as np
     import oracle
@@ -121,6 +152,7 @@ def cpu_baseline(inp, max_seconds: float = 30.0):
                    inp.initial_state, p.lengths, p.packed, tasks=tasks, workers=workers)
     dt = time.perf_counter() - t
     return {"value": th / dt, "unit": "token-heads/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"FP64 oracle forward of {len(tasks)} of {p.N * p.Hv} (sequence, head) "
                       f"tasks = {th} token-heads, {dt:.2f} s wall on {workers} processes"}
 
@@ -139,6 +171,14 @@ def main():
                          "sustained clocks before the warm-up and timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain copies of 1 GiB (counter calibration)")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="before each timed step, read a buffer of this many MB so that L2 "
+                         "and the 256 MB Infinity Cache hold nothing of the step's inputs "
+                         "(read, not written: a written buffer leaves dirty lines whose "
+                         "write-back would compete with the timed kernels)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the secondary lines (other workloads, tape-less forward, "
+                         "cold plan, inference, records context)")
     ap.add_argument("--infer-only", action="store_true",
                     help="only time kda_infer (decode and prefill) on the packed workload's heads, "
                          "for per-kernel profiles of the inference routes")
@@ -205,9 +245,13 @@ def main():
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    flush = torch.zeros(max(args.flush_mb, 0) << 18, dtype=torch.float32, device=dev)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush.numel():
+            torch.amax(flush, dim=0, out=flush_out)   # evicts the caches before the timed forward
         ev[i][0].record(stream)
         fwd()
         ev[i][1].record(stream)
@@ -228,10 +272,14 @@ def main():
     algo = algorithmic_fwd_bytes(p)
     achieved = algo / (fwd_mean * 1e-3) / 1e9
     traffic = recorded_traffic() if (route == 1 and p.name == "packed") else None
+    copy_gbs = copy_bandwidth(stream)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": ROUTE_KERNELS.get(route, "?"),
-            "algorithmic_bytes_per_launch": algo, "avg_launch_ms": round(fwd_mean, 4)}
+            "algorithmic_bytes_per_launch": algo, "avg_launch_ms": round(fwd_mean, 4),
+            "copy_GBs_same_job": round(copy_gbs, 1),
+            "frac_of_copy": round(achieved / copy_gbs, 4),
+            "cache_flush_mb_before_each_step": args.flush_mb}
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -265,13 +313,120 @@ def main():
                       "frac_of_hbm_peak": round(ab / (bwd_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                       "kernels": ["fwd_chunk_kernel<rebuild>", "bwd_chunk_kernel",
                                   "bwd_param_reduce_kernel", "bwd_dqk_reduce_kernel"]}
-        if route == 1:
+        if route == 1 and not args.no_extra:
             out["records_context"] = records_context_step(kda, p, d, inp_cpu, args, stream)
-    if p.name == "packed":
+    if not args.no_extra:
+        out["fwd_tapeless"] = tapeless_forward(kda, p, d, inp_cpu, args, stream,
+                                               flush if flush.numel() else None)
+        out["cold_plan"] = cold_plan_call(kda, p, d, inp_cpu, stream)
+    del flush
+    if p.name == "packed" and not args.no_extra:
         out["inference"] = inference_steps(kda, p, d, inp_cpu, args, stream)
+        out["other_workloads"] = other_workloads(kda, args, stream)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp_cpu)
     print(json.dumps(out), flush=True)
+
+
+def _fwd_bwd_times(kda, prob, d, stream, steps, warmup, flush=None, bwd=True, ctx_none=False):
+    """Mean forward and backward milliseconds by HIP events on `stream`."""
+    import torch
+    o = torch.empty_like(d.v)
+    fs = torch.empty_like(d.initial_state)
+    ctx = None if ctx_none else torch.empty(kda.kda_fwd_ctx_bytes(prob), dtype=torch.uint8,
+                                            device="cuda")
+    if bwd:
+        ws = torch.empty(kda.kda_bwd_workspace_bytes(prob), dtype=torch.uint8, device="cuda")
+        grads = [torch.empty_like(t) for t in (d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias,
+                                               d.initial_state)]
+    h = stream.cuda_stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+    for i in range(warmup + steps):
+        if flush is not None:
+            torch.amax(flush, dim=0, out=flush_out)
+        if i >= warmup:
+            ev[i - warmup][0].record(stream)
+        kda.kda_fwd(prob, d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state, o, fs,
+                    ctx, h)
+        if i >= warmup:
+            ev[i - warmup][1].record(stream)
+        if bwd:
+            kda.kda_bwd(prob, d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state, ctx,
+                        d.do, d.dfinal_state, *grads, ws, h)
+        if i >= warmup:
+            ev[i - warmup][2].record(stream)
+    torch.cuda.synchronize()
+    f = sum(a.elapsed_time(b) for a, b, _ in ev) / steps
+    b = sum(b_.elapsed_time(c) for _, b_, c in ev) / steps if bwd else None
+    return f, b
+
+
+def tapeless_forward(kda, p, d, inp_cpu, args, stream, flush):
+    """The forward without a context (no tape written): o and the final state
+    only, as inference-style callers run it."""
+    prob = kda.make_problem(p.B, p.T, p.Hqk, p.Hv, p.N, d.cu_seqlens, inp_cpu.cu_seqlens,
+                            route=args.route)
+    f, _ = _fwd_bwd_times(kda, prob, d, stream, args.steps, args.warmup, flush, bwd=False,
+                          ctx_none=True)
+    algo = algorithmic_fwd_bytes(p)
+    gbs = algo / (f * 1e-3) / 1e9
+    return {"ms_mean": round(f, 4), "token_heads_per_s": round(p.token_heads / (f * 1e-3), 1),
+            "achieved_GBs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def cold_plan_call(kda, p, d, inp_cpu, stream):
+    """One forward on a length set the schedule cache has not seen (a new
+    tape interval makes a new schedule: host planning, a pinned host buffer,
+    a device buffer and its upload), against the same call once cached."""
+    import torch
+    ck = 512 + 16 * (int(time.time() * 1000) % 1000)   # a key no earlier call used
+    prob = kda.make_problem(p.B, p.T, p.Hqk, p.Hv, p.N, d.cu_seqlens, inp_cpu.cu_seqlens,
+                            checkpoint_every=ck)
+    o = torch.empty_like(d.v)
+    fs = torch.empty_like(d.initial_state)
+    h = stream.cuda_stream
+    res = {}
+    for name in ("cold", "warm"):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t = time.perf_counter()
+        a.record(stream)
+        kda.kda_fwd(prob, d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state, o, fs,
+                    None, h)
+        host_ms = (time.perf_counter() - t) * 1e3
+        b.record(stream)
+        torch.cuda.synchronize()
+        res[name] = {"host_call_ms": round(host_ms, 4), "gpu_ms": round(a.elapsed_time(b), 4)}
+    return res
+
+
+def other_workloads(kda, args, stream):
+    """The other workloads of the suite, each drawn on the device by the same
+    recipe (timing only): forward and backward means in the launch
+    configuration of the automatic route, with the forward's HBM fraction.
+    `packed_h12` is the packed workload's per-GPU share when its 96 heads are
+    split over 8 GPUs (8 x 1024 tokens, 12 heads: 96 tasks)."""
+    import torch
+    import workloads
+    res = {}
+    items = [("fixed", workloads.workload("fixed")), ("grouped", workloads.workload("grouped")),
+             ("mixed", workloads.workload("mixed")),
+             ("packed_h12", (workloads.Problem([1024] * 8, 12, 12, packed=True, name="packed_h12"), 3))]
+    for name, (p, seed) in items:
+        d = workloads.make_inputs_on_device(p, seed, "cuda")
+        prob = kda.make_problem(p.B, p.T, p.Hqk, p.Hv, p.N, d.cu_seqlens, d.extra["cu_seqlens_cpu"])
+        route = kda.kda_plan_query(prob)[0]
+        f, b = _fwd_bwd_times(kda, prob, d, stream, max(args.steps // 4, 3), 2)
+        gbs = algorithmic_fwd_bytes(p) / (f * 1e-3) / 1e9
+        bgbs = algorithmic_bwd_bytes(p) / (b * 1e-3) / 1e9
+        res[name] = {"tasks": p.N * p.Hv, "token_heads": p.token_heads,
+                     "route": ROUTE_NAMES.get(route, "?"),
+                     "fwd_ms_mean": round(f, 4), "fwd_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                     "bwd_ms_mean": round(b, 4), "bwd_frac_of_hbm_peak": round(bgbs / HBM_PEAK_GBS, 4)}
+        del d
+        torch.cuda.empty_cache()
+    return res
 
 
 def records_context_step(kda, p, d, inp_cpu, args, stream):
@@ -344,8 +499,11 @@ def inference_steps(kda, p, d, inp_cpu, args, stream):
     prob = kda.make_infer_problem(1, Nd, p.Hqk, p.Hv, Nd, Nd, cu, di.cu_seqlens,
                                   state_indices=idx, state_indices_cpu=idx_cpu)
 
+    # the chunked route takes only the in-kernel gate: timed with it (same sizes)
     prob_c = kda.make_infer_problem(1, Nd, p.Hqk, p.Hv, Nd, Nd, cu, di.cu_seqlens,
-                                    state_indices=idx, state_indices_cpu=idx_cpu, route=1)
+                                    state_indices=idx, state_indices_cpu=idx_cpu, route=1,
+                                    use_gate_in_kernel=True, lower_bound=-5.0)
+    A_c, dt_c = di.A_log.to(dev), di.dt_bias.to(dev)
     # the training count holds the FP32 state twice; the pool is BF16
     bf16_state = lambda prob: algorithmic_fwd_bytes(prob) - prob.N * prob.Hv * 2 * 128 * 128 * 2
     res["decode"] = _time_infer(lambda: kda.kda_infer(prob, *t, None, None, pool, o, h),
@@ -353,7 +511,7 @@ def inference_steps(kda, p, d, inp_cpu, args, stream):
     res["decode"]["workload"] = f"{Nd} sequences x 1 token, Hqk={p.Hqk}, Hv={p.Hv}, pool {Nd} slots"
     res["decode"]["kernel"] = "infer_token_kernel (the automatic route)"
     res["decode"]["chunk_route_ms_mean"] = _time_infer(
-        lambda: kda.kda_infer(prob_c, *t, None, None, pool, o, h), args, stream, Nd * p.Hv,
+        lambda: kda.kda_infer(prob_c, *t, A_c, dt_c, pool, o, h), args, stream, Nd * p.Hv,
         bf16_state(dp))["ms_mean"]
     # prefill
     pool2 = d.initial_state.to(torch.bfloat16)

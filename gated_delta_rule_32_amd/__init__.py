@@ -35,6 +35,7 @@ KDA_ERR_HIP = 12
 KDA_ERR_CAPTURE = 13
 ROUTE_AUTO, ROUTE_CHUNK, ROUTE_ROWSPLIT, ROUTE_SEGMENTS = 0, 1, 2, 3
 CONTEXT_TAPE, CONTEXT_RECORDS = 0, 1
+PRECISION_AUTO, PRECISION_FULL, PRECISION_FAST = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -51,7 +52,7 @@ class KdaProblem(ctypes.Structure):
         ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
         ("scale", ctypes.c_float), ("lower_bound", ctypes.c_float),
         ("route", ctypes.c_int32), ("checkpoint_every", ctypes.c_int32),
-        ("context", ctypes.c_int32),
+        ("context", ctypes.c_int32), ("precision", ctypes.c_int32),
     ]
 
 
@@ -142,7 +143,7 @@ def make_problem(B: int, T: int, Hqk: int, Hv: int, N: int,
                  cu_seqlens_cpu: Optional[torch.Tensor] = None,
                  scale: Optional[float] = None, lower_bound: float = -5.0,
                  route: int = ROUTE_AUTO, checkpoint_every: int = 0,
-                 context: int = CONTEXT_TAPE) -> KdaProblem:
+                 context: int = CONTEXT_TAPE, precision: int = PRECISION_AUTO) -> KdaProblem:
     p = KdaProblem()
     p.B, p.T, p.Hqk, p.Hv, p.N = int(B), int(T), int(Hqk), int(Hv), int(N)
     p.cu_seqlens = _ptr(cu_seqlens)
@@ -152,6 +153,7 @@ def make_problem(B: int, T: int, Hqk: int, Hv: int, N: int,
     p.route = int(route)
     p.checkpoint_every = int(checkpoint_every)
     p.context = int(context)
+    p.precision = int(precision)
     # the struct holds raw pointers: keep the tensors alive with it
     p._keep = (cu_seqlens, cu_seqlens_cpu)
     return p
@@ -299,7 +301,7 @@ class RecurrentKDATrainingContext:
 
 
 def _problem_from(q, v, cu_seqlens, cu_seqlens_cpu, scale, lower_bound, route, checkpoint_every,
-                  context=CONTEXT_TAPE):
+                  context=CONTEXT_TAPE, precision=PRECISION_AUTO):
     _require(q.dim() == 4 and v.dim() == 4, "q and v must be [B, T, H, 128]")
     B, T, Hqk, Dq = q.shape
     Hv = v.shape[2]
@@ -317,7 +319,7 @@ def _problem_from(q, v, cu_seqlens, cu_seqlens_cpu, scale, lower_bound, route, c
         _require(cu_seqlens_cpu is None, "cu_seqlens_cpu must be omitted for fixed layout")
         N = B
     return make_problem(B, T, Hqk, Hv, N, cu_seqlens, cu_seqlens_cpu, scale, lower_bound,
-                        route, checkpoint_every, context)
+                        route, checkpoint_every, context, precision)
 
 
 def recurrent_kda_training_forward(q, k, v, g, beta, A_log, dt_bias, initial_state,
@@ -325,14 +327,14 @@ def recurrent_kda_training_forward(q, k, v, g, beta, A_log, dt_bias, initial_sta
                                    final_state_out=None, context_out=None, *,
                                    cu_seqlens_cpu=None, route: int = ROUTE_AUTO,
                                    checkpoint_every: int = 0, save_context: bool = True,
-                                   context: int = CONTEXT_TAPE):
+                                   context: int = CONTEXT_TAPE, precision: int = PRECISION_AUTO):
     """Forward of the KDA training recurrence: returns (o, final_state, ctx).
     context: CONTEXT_TAPE (FP32 state tape; the backward rebuilds chunk
     states) or CONTEXT_RECORDS (every chunk's records; the backward reruns
     nothing, the context is about 39 KiB per 16 tokens and value head)."""
     dev = q.device
     p = _problem_from(q, v, cu_seqlens, cu_seqlens_cpu, scale, lower_bound, route,
-                      checkpoint_every, context)
+                      checkpoint_every, context, precision)
     B, T, Hqk, Hv, N = p.B, p.T, p.Hqk, p.Hv, p.N
     bf = torch.bfloat16
     _check_tensor("q", q, bf, (B, T, Hqk, 128), dev)

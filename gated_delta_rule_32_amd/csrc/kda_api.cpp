@@ -53,6 +53,7 @@ struct Prob {
     int route;      // resolved: 1 chunk, 2 rowsplit, 3 segment-parallel chunk
     int ck;         // tape interval
     int ctxmode;    // KDA_CONTEXT_TAPE or KDA_CONTEXT_RECORDS
+    int precision;  // kda_precision
     float scale;
     std::vector<int64_t> len;    // per sequence
     std::vector<int64_t> start;  // flattened token offset per sequence
@@ -111,6 +112,8 @@ kda_status validate(const kda_problem* p, Prob& out) {
         return fail(KDA_ERR_ROUTE, "unknown context kind %d", p->context);
     if (p->context == KDA_CONTEXT_RECORDS && (p->route == 2 || p->route == 3))
         return fail(KDA_ERR_ROUTE, "per-chunk records need the chunked route");
+    if (p->precision < KDA_PRECISION_AUTO || p->precision > KDA_PRECISION_FAST)
+        return fail(KDA_ERR_ROUTE, "unknown precision %d", p->precision);
 
     out = Prob{};
     out.B = p->B; out.T = p->T; out.Hqk = p->Hqk; out.Hv = p->Hv; out.N = p->N;
@@ -118,6 +121,7 @@ kda_status validate(const kda_problem* p, Prob& out) {
     out.packed = packed;
     out.ck = ck;
     out.ctxmode = p->context;
+    out.precision = p->precision;
     out.scale = want_scale;
     out.tokens = (int64_t)p->B * p->T;
     if (packed) {
@@ -177,6 +181,70 @@ std::vector<int32_t> lpt_order(const Prob& p) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Byte layout of a device schedule (one buffer): the task order, sequence
+// starts and lengths, tape and chunk offsets, and the segment list.
+struct PlanLayout {
+    size_t off_task = 0, off_start = 0, off_len = 0, off_tape = 0, off_chunk = 0, off_seg = 0;
+    size_t bytes = 0;
+};
+
+PlanLayout plan_layout(const Prob& p) {
+    PlanLayout l;
+    size_t off = 0;
+    l.off_task = off;  off = align256(off + sizeof(int32_t) * (size_t)p.num_tasks);
+    l.off_start = off; off = align256(off + sizeof(int64_t) * (size_t)p.N);
+    l.off_len = off;   off = align256(off + sizeof(int32_t) * (size_t)p.N);
+    l.off_tape = off;  off = align256(off + sizeof(int64_t) * (size_t)(p.N + 1));
+    l.off_chunk = off; off = align256(off + sizeof(int64_t) * (size_t)(p.N + 1));
+    l.off_seg = off;   off = align256(off + sizeof(int32_t) * 2 * (size_t)p.total_segs);
+    l.bytes = off;
+    return l;
+}
+
+// Writes the schedule of `p` into `h` (l.bytes bytes, host memory).
+void fill_plan(const Prob& p, const PlanLayout& l, char* h) {
+    std::memset(h, 0, l.bytes);
+    std::vector<int32_t> order = lpt_order(p);
+    std::memcpy(h + l.off_task, order.data(), sizeof(int32_t) * order.size());
+    int64_t* st = (int64_t*)(h + l.off_start);
+    int32_t* ln = (int32_t*)(h + l.off_len);
+    int64_t* to = (int64_t*)(h + l.off_tape);
+    int64_t* co = (int64_t*)(h + l.off_chunk);
+    int32_t* sg = (int32_t*)(h + l.off_seg);
+    to[0] = 0;
+    co[0] = 0;
+    int64_t si = 0;
+    // segments in longest-first order of their sequences
+    std::vector<int> seqs(p.N);
+    for (int n = 0; n < p.N; ++n) {
+        seqs[n] = n;
+        st[n] = p.start[n];
+        ln[n] = (int32_t)p.len[n];
+        to[n + 1] = to[n] + (p.len[n] + p.ck - 1) / p.ck - 1;
+        co[n + 1] = co[n] + (p.len[n] + kChunk - 1) / kChunk;
+    }
+    std::stable_sort(seqs.begin(), seqs.end(), [&](int a, int b) { return p.len[a] > p.len[b]; });
+    for (int n : seqs) {
+        const int64_t nseg = (p.len[n] + p.ck - 1) / p.ck;
+        for (int64_t j = 0; j < nseg; ++j) {
+            sg[2 * si] = n;
+            sg[2 * si + 1] = (int32_t)j;
+            ++si;
+        }
+    }
+}
+
+kda::DevPlan dev_plan_at(const void* dev, const PlanLayout& l) {
+    const char* d = (const char*)dev;
+    kda::DevPlan p;
+    p.task = (const int32_t*)(d + l.off_task);
+    p.seq_start = (const int64_t*)(d + l.off_start);
+    p.seq_len = (const int32_t*)(d + l.off_len);
+    p.tape_off = (const int64_t*)(d + l.off_tape);
+    p.chunk_off = (const int64_t*)(d + l.off_chunk);
+    return p;
+}
+
 // ---------------------------------------------------------------------------
 // Device schedule cache
 // ---------------------------------------------------------------------------
@@ -191,8 +259,7 @@ struct PlanEntry {
     // the last use on each stream that launched with it (events recorded
     // after the launches; all complete means no queued kernel reads it)
     std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
-    size_t off_task = 0, off_start = 0, off_len = 0, off_tape = 0, off_chunk = 0, off_seg = 0;
-    size_t bytes = 0;
+    PlanLayout lay;
 };
 
 std::mutex g_mu;
@@ -326,48 +393,13 @@ kda_status get_plan(const Prob& p, hipStream_t stream, int dev, PlanLease& lease
         std::unique_ptr<PlanEntry>& e;
         ~Guard() { if (e) free_plan(e.get()); }
     } guard{ent};
-    size_t off = 0;
-    ent->off_task = off;  off = align256(off + sizeof(int32_t) * (size_t)p.num_tasks);
-    ent->off_start = off; off = align256(off + sizeof(int64_t) * (size_t)p.N);
-    ent->off_len = off;   off = align256(off + sizeof(int32_t) * (size_t)p.N);
-    ent->off_tape = off;  off = align256(off + sizeof(int64_t) * (size_t)(p.N + 1));
-    ent->off_chunk = off; off = align256(off + sizeof(int64_t) * (size_t)(p.N + 1));
-    ent->off_seg = off;   off = align256(off + sizeof(int32_t) * 2 * (size_t)p.total_segs);
-    ent->bytes = off;
-    e = hipHostMalloc(&ent->host, ent->bytes, hipHostMallocDefault);
+    ent->lay = plan_layout(p);
+    e = hipHostMalloc(&ent->host, ent->lay.bytes, hipHostMallocDefault);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(schedule)");
-    char* h = (char*)ent->host;
-    std::vector<int32_t> order = lpt_order(p);
-    std::memcpy(h + ent->off_task, order.data(), sizeof(int32_t) * order.size());
-    int64_t* st = (int64_t*)(h + ent->off_start);
-    int32_t* ln = (int32_t*)(h + ent->off_len);
-    int64_t* to = (int64_t*)(h + ent->off_tape);
-    int64_t* co = (int64_t*)(h + ent->off_chunk);
-    int32_t* sg = (int32_t*)(h + ent->off_seg);
-    to[0] = 0;
-    co[0] = 0;
-    int64_t si = 0;
-    // segments in longest-first order of their sequences
-    std::vector<int> seqs(p.N);
-    for (int n = 0; n < p.N; ++n) {
-        seqs[n] = n;
-        st[n] = p.start[n];
-        ln[n] = (int32_t)p.len[n];
-        to[n + 1] = to[n] + (p.len[n] + p.ck - 1) / p.ck - 1;
-        co[n + 1] = co[n] + (p.len[n] + kChunk - 1) / kChunk;
-    }
-    std::stable_sort(seqs.begin(), seqs.end(), [&](int a, int b) { return p.len[a] > p.len[b]; });
-    for (int n : seqs) {
-        const int64_t nseg = (p.len[n] + p.ck - 1) / p.ck;
-        for (int64_t j = 0; j < nseg; ++j) {
-            sg[2 * si] = n;
-            sg[2 * si + 1] = (int32_t)j;
-            ++si;
-        }
-    }
-    e = hipMalloc(&ent->dev, ent->bytes);
+    fill_plan(p, ent->lay, (char*)ent->host);
+    e = hipMalloc(&ent->dev, ent->lay.bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(schedule)");
-    e = hipMemcpyAsync(ent->dev, ent->host, ent->bytes, hipMemcpyHostToDevice, stream);
+    e = hipMemcpyAsync(ent->dev, ent->host, ent->lay.bytes, hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(schedule)");
     e = hipEventCreateWithFlags(&ent->ready, hipEventDisableTiming);
     if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
@@ -382,16 +414,7 @@ kda_status get_plan(const Prob& p, hipStream_t stream, int dev, PlanLease& lease
     return KDA_OK;
 }
 
-kda::DevPlan dev_plan(const PlanEntry* e) {
-    const char* d = (const char*)e->dev;
-    kda::DevPlan p;
-    p.task = (const int32_t*)(d + e->off_task);
-    p.seq_start = (const int64_t*)(d + e->off_start);
-    p.seq_len = (const int32_t*)(d + e->off_len);
-    p.tape_off = (const int64_t*)(d + e->off_tape);
-    p.chunk_off = (const int64_t*)(d + e->off_chunk);
-    return p;
-}
+kda::DevPlan dev_plan(const PlanEntry* e) { return dev_plan_at(e->dev, e->lay); }
 
 // ---------------------------------------------------------------------------
 // Context records (what kda_bwd checks)
@@ -475,17 +498,21 @@ std::vector<Span> input_spans(const Prob& p, const void* q, const void* k, const
             {cu, cu ? (size_t)(p.N + 1) * 8 : 0, "cu_seqlens"}};
 }
 
-kda::FwdArgs make_fwd_args(const Prob& p, const PlanEntry* plan, const void* q, const void* k,
+kda::FwdArgs make_fwd_args(const Prob& p, const kda::DevPlan& plan, const void* q, const void* k,
                            const void* v, const void* g, const void* beta, const float* A_log,
                            const float* dt_bias, const float* s0) {
     kda::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.A_log = A_log; a.dt_bias = dt_bias; a.s0 = s0;
-    a.plan = dev_plan(plan);
+    a.plan = plan;
     a.Hqk = p.Hqk; a.Hv = p.Hv; a.G = p.G;
     a.num_tasks = (int)p.num_tasks;
     a.ck_every = p.ck;
     a.scale = p.scale;
+    // log2-domain decay sum above which a chunk runs precise: ln(exp(-2))
+    a.precise_log2 = p.precision == KDA_PRECISION_FULL   ? -INFINITY
+                     : p.precision == KDA_PRECISION_FAST ? 1.0f
+                                                         : -2.0f * 1.4426950408889634f;
     return a;
 }
 
@@ -580,11 +607,15 @@ kda_status kda_plan_query(const kda_problem* pp, int32_t* route, int64_t* num_ta
     return KDA_OK;
 }
 
-kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const void* v,
-                   const void* g, const void* beta, const float* A_log, const float* dt_bias,
-                   const float* initial_state, void* o, float* final_state, void* ctx,
-                   size_t ctx_bytes, void* stream_) {
-    Prob p;
+}  // extern "C"
+
+namespace {
+
+// kda_fwd's checks, before any device access.
+kda_status fwd_check(const kda_problem* pp, Prob& p, const void* q, const void* k, const void* v,
+                     const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                     const float* initial_state, void* o, float* final_state, void* ctx,
+                     size_t ctx_bytes) {
     kda_status s = validate(pp, p);
     if (s != KDA_OK) return s;
     if (!q || !k || !v || !g || !beta || !A_log || !dt_bias || !initial_state || !o || !final_state)
@@ -599,19 +630,18 @@ kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const vo
     const size_t st = (size_t)p.N * p.Hv * kStateElems * 4;
     std::vector<Span> outs = {{o, tv, "o"}, {final_state, st, "final_state"},
                               {ctx, ctx ? ctx_bytes : 0, "ctx"}};
-    s = check_overlap(outs, ins);
-    if (s != KDA_OK) return s;
+    return check_overlap(outs, ins);
+}
 
-    hipStream_t stream = (hipStream_t)stream_;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    PlanLease lease;
-    s = get_plan(p, stream, dev, lease);
-    if (s != KDA_OK) return s;
-    const PlanEntry* plan = lease.ent;
-
-    kda::FwdArgs a = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, initial_state);
+// The training forward's launches over a schedule at `plan_dev` (layout
+// `lay`), and the host record of the context it fills.
+kda_status fwd_launch(const Prob& p, int dev, const void* plan_dev, const PlanLayout& lay,
+                      const void* q, const void* k, const void* v, const void* g,
+                      const void* beta, const float* A_log, const float* dt_bias,
+                      const float* initial_state, void* o, float* final_state, void* ctx,
+                      size_t ctx_bytes, hipStream_t stream) {
+    kda::FwdArgs a = make_fwd_args(p, dev_plan_at(plan_dev, lay), q, k, v, g, beta, A_log, dt_bias,
+                                   initial_state);
     a.o = o;
     a.s_final = final_state;
     a.tape = nullptr;
@@ -623,9 +653,10 @@ kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const vo
     } else if (ctx != nullptr) {
         a.tape = (float*)((char*)ctx + 256);
     }
+    hipError_t e;
     if (p.route == 3 && ctx != nullptr) {
         // segment-parallel: segment tasks; P and Q in the context after the tape
-        a.plan.task = (const int32_t*)((const char*)plan->dev + plan->off_seg);
+        a.plan.task = (const int32_t*)((const char*)plan_dev + lay.off_seg);
         a.seg_out = (float*)((char*)ctx + seg_scratch_off(p));
         a.seg_items = p.total_segs * p.Hv;
         e = kda::launch_fwd_segments(a, p.N, stream);
@@ -655,6 +686,29 @@ kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const vo
         g_ctx[ctx] = r;
     }
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const void* v,
+                   const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                   const float* initial_state, void* o, float* final_state, void* ctx,
+                   size_t ctx_bytes, void* stream_) {
+    Prob p;
+    kda_status s = fwd_check(pp, p, q, k, v, g, beta, A_log, dt_bias, initial_state, o, final_state,
+                             ctx, ctx_bytes);
+    if (s != KDA_OK) return s;
+    hipStream_t stream = (hipStream_t)stream_;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    PlanLease lease;
+    s = get_plan(p, stream, dev, lease);
+    if (s != KDA_OK) return s;
+    return fwd_launch(p, dev, lease.ent->dev, lease.ent->lay, q, k, v, g, beta, A_log, dt_bias,
+                      initial_state, o, final_state, ctx, ctx_bytes, stream);
 }
 
 kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const void* v,
@@ -690,6 +744,11 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
         if (r.key != plan_key(p, dev) || r.B != p.B || r.T != p.T || r.Hqk != p.Hqk ||
             r.Hv != p.Hv || r.N != p.N || r.ctxmode != p.ctxmode)
             return fail(KDA_ERR_CTX_MISMATCH, "context was made for another shape or device");
+        // the backward reads what its route's forward stored (the
+        // segment-parallel one also reads P^T after the tape)
+        if (r.route != p.route)
+            return fail(KDA_ERR_CTX_MISMATCH, "context was filled on route %d, the backward resolves to %d",
+                        r.route, p.route);
         if (std::memcmp(r.ptrs, ptrs, sizeof(ptrs)) != 0)
             return fail(KDA_ERR_CTX_MISMATCH, "inputs differ from the forward that made the context");
         if (r.stream != stream)
@@ -718,7 +777,7 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
     const PlanEntry* plan = lease.ent;
 
     kda::BwdArgs b{};
-    b.f = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, initial_state);
+    b.f = make_fwd_args(p, dev_plan(plan), q, k, v, g, beta, A_log, dt_bias, initial_state);
     char* ws = (char*)workspace;
     const bool records = p.ctxmode == KDA_CONTEXT_RECORDS;
     if (records) {  // the forward stored every chunk's records in the context
@@ -742,7 +801,7 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
     if (!records) {
         // segment list sits after the chunk offsets in the schedule
         kda::FwdArgs rb = b.f;
-        rb.plan.task = (const int32_t*)((const char*)plan->dev + plan->off_seg);
+        rb.plan.task = (const int32_t*)((const char*)plan->dev + plan->lay.off_seg);
         e = kda::launch_state_rebuild(rb, p.total_segs * p.Hv, stream);
         if (e != hipSuccess) return hip_fail(e, "state rebuild launch");
     }
@@ -750,7 +809,7 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
     if (p.route == 3 && !records) {
         // segment-parallel adjoint over the tape segments, with the forward's P
         kda::BwdArgs bs = b;
-        bs.f.plan.task = (const int32_t*)((const char*)plan->dev + plan->off_seg);
+        bs.f.plan.task = (const int32_t*)((const char*)plan->dev + plan->lay.off_seg);
         bs.f.seg_items = p.total_segs * p.Hv;
         bs.seg_p = (const float*)((const char*)ctx + seg_scratch_off(p) +
                                   2 * (size_t)p.total_segs * p.Hv * kStateElems * sizeof(float));  // P^T
@@ -790,8 +849,15 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
     for (int32_t f : {ip->use_qk_l2norm, ip->use_gate_in_kernel, ip->beta_is_logit})
         if (f != 0 && f != 1) return fail(KDA_ERR_SHAPE, "option flags must be 0 or 1 (got %d)", f);
     if (ip->route < 0 || ip->route > 2) return fail(KDA_ERR_ROUTE, "unknown route %d", ip->route);
+    // the chunk factors exp(+-gc) need every per-token log-decay >= -5: true
+    // for the in-kernel gate with such a lower bound, unknown for a log-space
+    // gate given as is (the host never reads g), which therefore runs token by
+    // token
     const bool bounded_gate = ip->use_gate_in_kernel && ip->lower_bound >= -5.0f;
-    if (ip->route == KDA_ROUTE_CHUNK && ip->use_gate_in_kernel && !bounded_gate)
+    if (ip->route == KDA_ROUTE_CHUNK && !ip->use_gate_in_kernel)
+        return fail(KDA_ERR_ROUTE,
+                    "the chunked route needs the in-kernel gate (a log-space gate is not bounded below)");
+    if (ip->route == KDA_ROUTE_CHUNK && !bounded_gate)
         return fail(KDA_ERR_ROUTE, "the chunked route needs lower_bound >= -5 (got %g)",
                     (double)ip->lower_bound);
     if (ip->use_gate_in_kernel) {
@@ -909,7 +975,7 @@ kda_status kda_infer(const kda_infer_problem* ip, const void* q, const void* k, 
     s = get_plan(p, stream, dev, lease);
     if (s != KDA_OK) return s;
     const PlanEntry* plan = lease.ent;
-    kda::FwdArgs a = make_fwd_args(p, plan, q, k, v, g, beta, A_log, dt_bias, nullptr);
+    kda::FwdArgs a = make_fwd_args(p, dev_plan(plan), q, k, v, g, beta, A_log, dt_bias, nullptr);
     const int64_t longest = *std::max_element(p.len.begin(), p.len.end());
     const int route = ip->route != KDA_ROUTE_AUTO ? ip->route
                       : (bounded_gate && longest > 1 && S == 0) ? KDA_ROUTE_CHUNK : KDA_ROUTE_ROWSPLIT;

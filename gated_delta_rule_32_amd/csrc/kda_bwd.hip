@@ -33,10 +33,14 @@
 // U, T, Akk and Aqk' come from the records the state rebuild wrote.
 //
 // Precision.  Every product uses BF16 operands with FP32 accumulation except
-// dAqk' Ki and dAqk'^T Qg', whose contributions dQg'.Qg' and dKi.Ki to dg
-// cancel exactly for every token pair on the same side of t in the reverse
-// cumulative sum: with single BF16 operands the uncancelled rounding residue
-// dominates dlam, so both use three-product hi/lo splits (FP32-accurate).
+// the two pairs whose contributions to dg cancel exactly for every token pair
+// on the same side of t in the reverse cumulative sum: dAqk' Ki and
+// dAqk'^T Qg' (three-product hi/lo splits, FP32-accurate), and dAkk Ki and
+// dAkk^T Kg (Ki and Kg as hi/lo pairs against the same BF16 dAkk, so that
+// the two terms of each pair are the same product).  With single BF16
+// operands the uncancelled rounding residue dominates dlam, the more so the
+// weaker the decay (Akk's entries are then O(1)).  W = Tb Kg takes Kg's lo
+// part as well.
 #include <type_traits>
 
 #include "kda_chunk.hpp"
@@ -67,7 +71,8 @@ struct BwdLds {
     alignas(16) float dots[4][2][CH]; // per-wave partial row dots qn.dqn, kn.dkn
     alignas(16) bf16 cf_qh[8 * FS];   // CF(Qg') hi / lo
     alignas(16) bf16 cf_ql[8 * FS];
-    alignas(16) bf16 cf_kg[8 * FS];   // CF(Kg)
+    alignas(16) bf16 cf_kg[8 * FS];   // CF(Kg) hi / lo
+    alignas(16) bf16 cf_kgl[8 * FS];
     alignas(16) bf16 cf_kih[8 * FS];  // CF(Ki) hi / lo
     alignas(16) bf16 cf_kil[8 * FS];
     alignas(16) bf16 rf_kt[8 * FS];   // RF(Kt)
@@ -338,7 +343,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             *(float4*)&gC[4] = *(const float4*)&sm.gamc[c8 + 4];
             const float rq = sm.rqn[ci & 1][r] * scale;
             const float rk = sm.rkn[ci & 1][r];
-            bf16x4 qh4[2], ql4[2], kg4[2], kih4[2], kil4[2], kt4[2];
+            bf16x4 qh4[2], ql4[2], kg4[2], kgh4[2], kgl4[2], kih4[2], kil4[2], kt4[2];
 #pragma unroll
             for (int s4 = 0; s4 < 2; ++s4) {
                 f32x4 qg, kg, ki, kt;
@@ -354,8 +359,12 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                     ki[j] = kn * gin;
                     kt[j] = ki[j] * gC[i];
                 }
-                split4(qg, qh4[s4], ql4[s4]);
+                // rounded hi: the dS update uses it alone (a truncated hi
+                // would shrink dO^T Qg' by 2^-10 on average, and the shrink
+                // accumulates in dS as long as the decay keeps it)
+                split4_rne(qg, qh4[s4], ql4[s4]);
                 kg4[s4] = to_bf4(kg);
+                split4(kg, kgh4[s4], kgl4[s4]);
                 split4(ki, kih4[s4], kil4[s4]);
                 kt4[s4] = to_bf4(kt);
             }
@@ -367,7 +376,8 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
             }
             store_cf16(sm.cf_qh, r, c8, qh4[0], qh4[1]);
             store_cf16(sm.cf_ql, r, c8, ql4[0], ql4[1]);
-            store_cf16(sm.cf_kg, r, c8, kg4[0], kg4[1]);
+            store_cf16(sm.cf_kg, r, c8, kgh4[0], kgh4[1]);
+            store_cf16(sm.cf_kgl, r, c8, kgl4[0], kgl4[1]);
             store_cf16(sm.cf_kih, r, c8, kih4[0], kih4[1]);
             store_cf16(sm.cf_kil, r, c8, kil4[0], kil4[1]);
         }
@@ -546,7 +556,8 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 for (int i = 0; i < 4; ++i) dbk += dbkT[i] * kgr[i];
                 dKgT[j] = dbkT * sm.beta[ci & 1][cl];
                 // W = Tb Kg (CF): lane (gq, k) holds W[4gq + i][k]
-                wcf[j] = mma16(tbAb, ld4(&sm.cf_kg[(kb0 + j) * FS], lane), zero4());
+                wcf[j] = mma16(tbAb, ld4(&sm.cf_kgl[(kb0 + j) * FS], lane),
+                               mma16(tbAb, ld4(&sm.cf_kg[(kb0 + j) * FS], lane), zero4()));
             }
             dbk = xor_sum_gq(dbk);
             if (gq == 0) sm.dbp[1][wave][cl] = dbk;
@@ -602,7 +613,10 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                 const bf16x4 qh = ld4(&sm.cf_qh[(kb0 + j) * FS], lane);
                 const bf16x4 ql = ld4(&sm.cf_ql[(kb0 + j) * FS], lane);
                 dKgT[j] = mma16(kil, dAkkT, mma16(kih, dAkkT, dKgT[j]));  // + dAkk Ki
-                f32x4 x = mma16(ld4(&sm.cf_kg[(kb0 + j) * FS], lane), dAkkB, zero4());  // dAkk^T Kg
+                // dAkk^T Kg with Kg as a hi/lo pair: its dg terms cancel those of
+                // dAkk Ki (Ki hi/lo) pair by pair in the reverse sum
+                f32x4 x = mma16(ld4(&sm.cf_kgl[(kb0 + j) * FS], lane), dAkkB,
+                                mma16(ld4(&sm.cf_kg[(kb0 + j) * FS], lane), dAkkB, zero4()));
                 dKiT[j] = mma16_split(qh, ql, daqh, daql, x);             // + dAqk'^T Qg'
                 dQgT[j] = mma16_split(kih, kil, daqTh, daqTl, dQgT[j]);   // + dAqk' Ki
             }

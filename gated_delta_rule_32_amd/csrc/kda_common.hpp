@@ -94,6 +94,14 @@ __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
     lo = to_bf4(x - h);
 }
 
+// The same pair with hi rounded to nearest (unbiased, so that hi may also
+// serve alone as the operand's BF16 value): hi = bf16(x), lo = bf16(x - hi),
+// where x - hi is exact.
+__device__ __forceinline__ void split4_rne(f32x4 x, bf16x4& hi, bf16x4& lo) {
+    hi = to_bf4(x);
+    lo = to_bf4(x - from_bf4(hi));
+}
+
 // base + off elements with the byte offset formed in 32 bits, so that the
 // access can use a scalar base and a 32-bit vector offset instead of 64-bit
 // per-lane address arithmetic (off * sizeof(T) must stay below 2^32).

@@ -69,7 +69,10 @@ struct FwdLds {
     alignas(16) bf16 rf_qg[8 * FS];
     alignas(16) bf16 rf_kg[8 * FS];
     alignas(16) bf16 rf_ki[8 * FS];
+    alignas(16) bf16 rf_kg_lo[8 * FS];  // precise chunks: lo parts of Kg, Ki
+    alignas(16) bf16 rf_ki_lo[8 * FS];
     alignas(16) bf16 cf_kt[8 * FS2];  // CF(Kt) as [hi | lo] pairs, 8 bf16 per lane
+    int precise[2];                   // by chunk parity: the chunk runs precise
 };
 
 struct ColIn {   // V for the wave's 32 columns: RF(V)[2w], RF(V)[2w+1]
@@ -125,10 +128,11 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], 
 // that the backward reruns nothing.  kMode = kFwdInfer: the inference forward
 // of page "flashinfer.kda.recurrent_kda" (no tape): the state comes from a
 // BF16 pool slot and goes back to it, and the prologue follows the call's
-// options (L2 norm on or off, in-kernel gate with its lower bound or a
-// log-space gate as given, beta as a logit or as given).  The chunk form
-// needs every per-token log-decay at or above -5 (so that the factors
-// exp(+-gc) stay in range); the host routes other calls elsewhere.
+// options (L2 norm on or off, the in-kernel gate with its lower bound, beta as
+// a logit or as given).  The chunk form needs every per-token log-decay at or
+// above -5 (so that the factors exp(+-gc) stay in range), so the host sends
+// only the in-kernel gate with lower_bound >= -5 here; log-space gates run
+// token by token.
 // kFwdInferCkpt is the same with state checkpoints (a separate instance, so
 // that the plain one keeps its registers).  kFwdSegPQ and kFwdSegOut make the
 // segment-parallel training forward for calls with few tasks: each tape
@@ -228,15 +232,14 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     }
 
     // prologue options (inference only; the training modes fix them)
-    const bool gate_in = !kInfer || a.use_gate_in_kernel != 0;
     const bool l2norm = !kInfer || a.use_qk_l2norm != 0;
     const bool beta_logit = !kInfer || a.beta_is_logit != 0;
     const float lb2 = (kInfer ? a.lower_bound : -5.0f) * LOG2E;  // log2-domain lower bound
-    const float eA = gate_in ? __expf(a.A_log[h]) : 0.f;
+    const float eA = __expf(a.A_log[h]);
     // z*log2(e) = g*(eA log2e) + dt*(eA log2e); the log2-domain decay is
     // -5 log2(e) sigmoid(z)
     const float zs = eA * LOG2E;
-    if (tid < D) sm.dtz[tid] = (gate_in && a.dt_bias != nullptr) ? a.dt_bias[h * D + tid] * zs : 0.f;
+    if (tid < D) sm.dtz[tid] = a.dt_bias != nullptr ? a.dt_bias[h * D + tid] * zs : 0.f;
 
     SeqPtrs sp;
     sp.q = (const bf16*)a.q + (tok0 * a.Hqk + hq) * D;
@@ -288,17 +291,16 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         *(float4*)&dz[4] = *(const float4*)&sm.dtz[c8 + 4];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            if (kInfer && !gate_in) {  // a log-space decay as given
-                lv[i] = (LOG2E * vm) * (float)cur.g[i];
-            } else {
-                const float e = __builtin_amdgcn_exp2f(-((float)cur.g[i] * zs + dz[i]));
-                lv[i] = (lb2 * vm) * __builtin_amdgcn_rcpf(1.0f + e);
-            }
+            const float e = __builtin_amdgcn_exp2f(-((float)cur.g[i] * zs + dz[i]));
+            lv[i] = (lb2 * vm) * __builtin_amdgcn_rcpf(1.0f + e);
         }
         *(float4*)&sm.lam[r][c8] = make_float4(lv[0], lv[1], lv[2], lv[3]);
         *(float4*)&sm.lam[r][c8 + 4] = make_float4(lv[4], lv[5], lv[6], lv[7]);
         // the row's 16 lanes store the same value (no branch)
         sm.beta[ci & 1][r] = vm * (beta_logit ? sigmoidf_((float)cur.b) : (float)cur.b);
+        // chunk ci's precision flag, set by phase B after the next barrier
+        // (its slot last served chunk ci-2, which every wave has finished)
+        if (tix == 0) sm.precise[ci & 1] = 0;
     };
     // ---- B: in-place prefix sums of chunk ci's decays over its tokens, and
     // exp(gC).  Every wave takes 32 channels: lanes 0-31 sum rows 0-7, lanes
@@ -327,6 +329,9 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         for (int i = 0; i < 8; ++i) sm.lam[r0 + i][ch] = x[i] + off;
         // both halves hold the chunk total: the pair stores the same value
         sm.gamc[ci & 1][ch] = __builtin_amdgcn_exp2f(x[7] + other);
+        // a channel that keeps more than exp(-2) of its state over the chunk
+        // makes the chunk precise (every lane that sees one stores the same 1)
+        if (x[7] + other > a.precise_log2) sm.precise[ci & 1] = 1;
     };
     float rq, rk;   // 1/sqrt(128)/|q| and 1/|k| of the chunk's row
     phase_a(cb, rq, rk);
@@ -374,6 +379,14 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         }
 
         __syncthreads();   // chunk ci's prefix sums, exp(gC) and beta are in LDS
+        // Precise chunk (some channel keeps more than exp(-2) of its state
+        // over it): the operands that predict the state, Kg, Ki and S0, and Y
+        // in Tb Y, become BF16 hi/lo pairs as well (three products each), so
+        // that with weak decay the rounding of the prediction does not pile
+        // up in the carried state.  The flag is uniform over the workgroup,
+        // and the backward's rebuild takes the same decisions as the forward,
+        // so it reproduces the forward's chunk states exactly.
+        const bool precise = __builtin_amdgcn_readfirstlane(sm.precise[ci & 1]) != 0;
         // ---- C: decay factors and the chunk's operands ----
         {
             float gc[8], gC[8];
@@ -398,8 +411,17 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                     kt[j] = ki[j] * gC[i];
                 }
                 qg4[s4] = to_bf4(qg);
-                kg4[s4] = to_bf4(kg);
-                ki4[s4] = to_bf4(ki);
+                if (precise) {
+                    bf16x4 kl, il;
+                    split4(kg, kg4[s4], kl);
+                    split4(ki, ki4[s4], il);
+                    const int o = rf_off(r, c8) + 64 * s4;
+                    *(bf16x4*)&sm.rf_kg_lo[o] = kl;
+                    *(bf16x4*)&sm.rf_ki_lo[o] = il;
+                } else {
+                    kg4[s4] = to_bf4(kg);
+                    ki4[s4] = to_bf4(ki);
+                }
                 split4(kt, th4[s4], tl4[s4]);
             }
             const int orf = rf_off(r, c8);  // channels c8+4.. sit one lane group later
@@ -433,6 +455,39 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         f32x4 Y[2] = {zero4(), zero4()};
         f32x4 OT[2] = {zero4(), zero4()};
         auto y_ot = [&]() __attribute__((always_inline)) {
+            if (precise) {
+                // Y = Kg_hi S0_hi + Kg_hi S0_lo + Kg_lo S0_hi, O^T from S0_hi
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
+                    const bf16x8 kl8 = cat8(ld4(&sm.rf_kg_lo[(2 * j) * FS], lane),
+                                            ld4(&sm.rf_kg_lo[(2 * j + 1) * FS], lane));
+                    bf16x8 q8;
+                    if constexpr (kOut)
+                        q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
+#pragma unroll
+                    for (int vb = 0; vb < 2; ++vb) {
+                        if constexpr (kRec) {
+                            const bf16x4 ident = identity_frag(lane);
+                            const int vbg = 2 * wave + vb;
+                            bf16* dst = (bf16*)a.rec_s0 + rec * (D * D) + lane * 4;
+                            *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) =
+                                to_bf4(transpose_frag(to_bf4(S[2 * j][vb]), ident));
+                            *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) =
+                                to_bf4(transpose_frag(to_bf4(S[2 * j + 1][vb]), ident));
+                        }
+                        bf16x4 h0, l0, h1, l1;
+                        split4(S[2 * j][vb], h0, l0);
+                        split4(S[2 * j + 1][vb], h1, l1);
+                        const bf16x8 sh = cat8(h0, h1);
+                        Y[vb] = mma32(kg8, sh, Y[vb]);
+                        Y[vb] = mma32(kg8, cat8(l0, l1), Y[vb]);
+                        Y[vb] = mma32(kl8, sh, Y[vb]);
+                        if constexpr (kOut) OT[vb] = mma32(sh, q8, OT[vb]);
+                    }
+                }
+                return;
+            }
             bf16x8 sb[4][2];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -472,6 +527,12 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
                 const bf16x8 ki8 = cat8(ld4(&sm.rf_ki[(2 * j) * FS], lane), ld4(&sm.rf_ki[(2 * j + 1) * FS], lane));
                 akk = mma32(kg8, ki8, akk);     // lane (gq, c) holds Akk[4gq+i][c]
+                if (precise) {                  // + Kg_hi Ki_lo + Kg_lo Ki_hi
+                    akk = mma32(kg8, cat8(ld4(&sm.rf_ki_lo[(2 * j) * FS], lane),
+                                          ld4(&sm.rf_ki_lo[(2 * j + 1) * FS], lane)), akk);
+                    akk = mma32(cat8(ld4(&sm.rf_kg_lo[(2 * j) * FS], lane),
+                                     ld4(&sm.rf_kg_lo[(2 * j + 1) * FS], lane)), ki8, akk);
+                }
             }
             y_ot();
             const float4 b4 = *(const float4*)&sm.beta[ci & 1][4 * gq];
@@ -579,9 +640,19 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             // (every operand tuple is formed where it is produced, no copies)
             const bf16x8 tb2 = cat8(tbh, tbl);
             U[0] = mma32(tb2, cat8(cfv0, cfv0), zero4());
-            U[0] = mma32(tb2, cat8(to_bf4_neg(Y[0]), to_bf4_neg(Y[0])), U[0]);
             U[1] = mma32(tb2, cat8(cfv1, cfv1), zero4());
-            U[1] = mma32(tb2, cat8(to_bf4_neg(Y[1]), to_bf4_neg(Y[1])), U[1]);
+            if (precise) {   // Y as a hi/lo pair as well: [Tb_hi|Tb_lo] [-Y_hi;-Y_hi] + [-Y_lo;-Y_lo]
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) {
+                    bf16x4 yh, yl;
+                    split4(-Y[vb], yh, yl);
+                    U[vb] = mma32(tb2, cat8(yh, yh), U[vb]);
+                    U[vb] = mma32(tb2, cat8(yl, yl), U[vb]);
+                }
+            } else {
+                U[0] = mma32(tb2, cat8(to_bf4_neg(Y[0]), to_bf4_neg(Y[0])), U[0]);
+                U[1] = mma32(tb2, cat8(to_bf4_neg(Y[1]), to_bf4_neg(Y[1])), U[1]);
+            }
         }
         load_cols_s(vcur, sp, min(t0 + CH + cl, L - 1), 32 * wave + 4 * gq);
         // O^T += U^T Aqk^T, store; then S update.  U as [hi|hi] and [lo|lo]

@@ -44,6 +44,10 @@ struct FwdArgs {
     int num_tasks;
     int ck_every;           // tape interval (tokens), multiple of 16
     float scale;
+    // Chunked kernels: a chunk in which some channel's log2-domain decay sum
+    // exceeds precise_log2 runs with hi/lo operands on its whole state path
+    // (-inf: every chunk; above 0: none).
+    float precise_log2;
     // Inference (infer_token_kernel): prologue options and the BF16 state
     // pool [pool_slots][Hv][128][128] read and written in place at slot
     // pool_index[n] (slot n when pool_index is null); s0, s_final and tape

@@ -125,6 +125,23 @@ typedef enum {
     KDA_CONTEXT_RECORDS = 1
 } kda_context;
 
+/* Precision of the chunked kernels' state path.  The chunk form predicts the
+ * state against each chunk's keys with BF16 MFMA operands (Kg S0^T, Tb Y, Akk);
+ * under decay that rounding is forgotten within a few tokens, but a channel
+ * whose decay is weak keeps it, and the FP32 state drifts past 1e-3.  AUTO
+ * runs a chunk with BF16 hi/lo pairs on those operands too (three products
+ * each, FP32-accurate) when some channel keeps more than exp(-2) of its state
+ * over the chunk (the accurate full-precision-state recurrence of page
+ * "flashinfer.kda_training", paragraph 5, here per chunk and only where the
+ * decay makes it matter); FULL runs every chunk that way; FAST none (final
+ * states can then miss 1e-3 on weakly decaying inputs).  The row-split route
+ * is FP32 throughout and ignores this. */
+typedef enum {
+    KDA_PRECISION_AUTO = 0,
+    KDA_PRECISION_FULL = 1,
+    KDA_PRECISION_FAST = 2
+} kda_precision;
+
 /* One call's shape.  All fields are read by value; the struct is not kept. */
 typedef struct {
     int32_t B;                       /* physical batch (1 when packed) */
@@ -139,6 +156,7 @@ typedef struct {
     int32_t route;                   /* kda_route; AUTO unless testing a route */
     int32_t checkpoint_every;        /* tape interval in tokens; 0 selects 256; a multiple of 16 */
     int32_t context;                 /* kda_context: what the forward saves for the backward */
+    int32_t precision;               /* kda_precision; AUTO unless testing */
 } kda_problem;
 
 /* Library version (KDA_VERSION). */
@@ -227,11 +245,11 @@ kda_status kda_bwd(const kda_problem* p,
  * runs in FP32 between the pool's load and store.
  * route: KDA_ROUTE_ROWSPLIT (2) runs the token-serial kernel, exact for any
  * gate; KDA_ROUTE_CHUNK (1) runs the chunked MFMA kernel, which needs every
- * per-token log-decay to be >= -5 (always true for the in-kernel gate with
- * lower_bound >= -5; for a log-space gate the caller vouches for it, as a
- * smaller one overflows the chunk factors); KDA_ROUTE_AUTO (0) takes the
- * chunked kernel for the in-kernel gate with lower_bound >= -5 when some
- * sequence is longer than one token, else the token-serial one.
+ * per-token log-decay to be >= -5, so it is accepted only for the in-kernel
+ * gate with lower_bound >= -5 (a log-space gate given as is has no bound the
+ * host can check; KDA_ERR_ROUTE); KDA_ROUTE_AUTO (0) takes the chunked kernel
+ * for the in-kernel gate with lower_bound >= -5 when some sequence is longer
+ * than one token, else the token-serial one.
  * State checkpoints (parameters state_checkpoints, checkpoint_cu_starts,
  * checkpoint_every_n_tokens): with checkpoint_every = E > 0 (a multiple of
  * 16), sequence n stores ceil(L_n / E) BF16 states [Hv][128][128] into rows

@@ -234,6 +234,9 @@ def test_infer_rejections_before_device_work():
     # routes: unknown, or the chunked one with a gate it cannot bound
     assert call(prob(route=3)) == 11
     assert call(prob(use_gate_in_kernel=True, lower_bound=-6.0, route=1)) == 11
+    # a log-space gate (no bound the host can check) on the chunked route
+    assert call(prob(route=1)) == 11
+    assert call(prob(use_gate_in_kernel=False, route=1)) == 11
     # scale must be positive
     assert call(prob(scale=-1.0)) == 5
     # option flags are 0 or 1

@@ -49,7 +49,11 @@ def test_backward_small(case, route):
     _report_and_check(list(zip(NAMES, got, ref)))
 
 
-def _sampled(problem):
+def _sampled(problem, spread=24):
+    """Tasks the oracle runs: whole q/k-head groups (dq, dk sum over a group)
+    on `spread` (sequence, q/k head) pairs taken evenly along the longest-first
+    dispatch order plus the first/last (or longest/shortest) sequences, and
+    one value head over every sequence (dA_log, ddt_bias sum over them)."""
     G = problem.Hv // problem.Hqk
     hq = problem.Hqk // 2
     if problem.name == "mixed":
@@ -57,10 +61,16 @@ def _sampled(problem):
         seqs = [int(np.argmax(L)), int(np.argmin(L))]
     else:
         seqs = [0, problem.N - 1] if problem.N > 1 else [0]
-    group = [(n, hq * G + g) for n in seqs for g in range(G)]
+    pairs = {(n, hq) for n in seqs}
+    order = sorted(range(problem.N), key=lambda n: -problem.lengths[n])
+    qk_tasks = [(n, j) for n in order for j in range(problem.Hqk)]
+    for i in np.linspace(0, len(qk_tasks) - 1, min(spread, len(qk_tasks))):
+        pairs.add(qk_tasks[int(round(i))])
+    pairs = sorted(pairs)
+    group = [(n, j * G + g) for (n, j) in pairs for g in range(G)]
     h_par = hq * G
     every = [(n, h_par) for n in range(problem.N)]
-    return seqs, hq, h_par, sorted(set(group + every))
+    return pairs, h_par, sorted(set(group + every))
 
 
 @pytest.mark.parametrize("name", workloads.WORKLOADS)
@@ -68,8 +78,9 @@ def test_backward_workloads_sampled(name):
     inp = workloads.make_workload(name, with_adjoints=True)
     p = inp.problem
     G = p.Hv // p.Hqk
-    seqs, hq, h_par, tasks = _sampled(p)
-    print(f"[bwd] workload={name} tasks={len(tasks)} seqs={seqs} hq={hq} h_par={h_par}", flush=True)
+    pairs, h_par, tasks = _sampled(p)
+    print(f"[bwd] workload={name} AUTO tasks={len(tasks)} qk-groups={len(pairs)} h_par={h_par}",
+          flush=True)
     got = dict(zip(NAMES, _run_backward(inp)))
     res = oracle.backward_tasks(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.A_log, inp.dt_bias,
                                 inp.initial_state, inp.do, inp.dfinal_state, p.lengths, p.packed,
@@ -84,7 +95,7 @@ def test_backward_workloads_sampled(name):
                             ("dinitial_state", dS0, got["dinitial_state"][n, h])):
             cat[key][0].append(np.ravel(x))
             cat[key][1].append(np.ravel(ref))
-    for n in seqs:
+    for (n, hq) in pairs:
         b, t0, L = sl[n]
         s = slice(t0, t0 + L)
         for key, idx in (("dq", 0), ("dk", 1)):

@@ -3,7 +3,10 @@ C ABI, forward and backward against the FP64 oracle:
 
 * the strongest decay the gate allows (the gate saturates at the lower bound,
   lambda = -5 per token, so the in-chunk factors exp(+-gc) reach e^75);
-* no decay (the gate at 0: the state only accumulates);
+* no decay (the gate at 0: the state only accumulates) and weak decay
+  (alpha = 0.99 per token) over 300, 1024 and 4096 tokens: nothing forgets the
+  rounding of the chunk form's state predictions, so these hold the chunked
+  route's precise chunks to the FP32 state bar;
 * beta -> 1 (the delta rule recalls v exactly) and beta -> 0 (pure decay);
 * zero values and zero initial state (output and final state exactly zero);
 * eight value heads per q/k head;
@@ -38,6 +41,11 @@ CASES = {
     "max_decay": (P([40, 33], 2, 2, packed=True), 201, dict(g=8.0, A_log=2.0)),
     # z = e^2 (-30 + dt) ~ -222: sigmoid(z) = 0 to FP32, no decay over 300 tokens
     "no_decay": (P([300], 1, 2, packed=True), 202, dict(g=-30.0, A_log=2.0)),
+    # alpha = exp(-5 sigmoid(g)) with A_log = dt_bias = 0: g = -6.2 gives 0.99
+    "weak_decay_1024": (P([1024], 1, 2, packed=True), 209, dict(g=-6.2, A_log=0.0, dt_bias=0.0)),
+    "no_decay_1024": (P([1024], 1, 2, packed=True), 210, dict(g=-30.0, A_log=2.0)),
+    "weak_decay_4096": (P([4096], 1, 1, packed=True), 211, dict(g=-6.2, A_log=0.0, dt_bias=0.0)),
+    "no_decay_4096": (P([4096], 1, 1, packed=True), 212, dict(g=-30.0, A_log=2.0)),
     "beta_one": (P([50, 17], 2, 2, packed=True), 203, dict(beta=20.0)),
     "beta_zero": (P([50], 1, 2, packed=True), 204, dict(beta=-20.0)),
     "zero_values_state": (P([45, 16], 1, 2, packed=True), 205, dict(v=0.0, initial_state=0.0)),
@@ -46,13 +54,16 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("route", [1, 2], ids=["chunk", "rowsplit"])
+# route 3: the segment-parallel chunked route through a 64-token tape (it needs
+# the context), whose P and Q runs take the same precise chunks
+@pytest.mark.parametrize("route", [1, 2, 3], ids=["chunk", "rowsplit", "segments"])
 @pytest.mark.parametrize("case", list(CASES.keys()))
 def test_forward_edge(case, route):
     problem, seed, set_to = CASES[case]
     inp = _inputs(problem, seed, **set_to)
     print(f"[edge fwd] case={case} route={route} lengths={problem.lengths}", flush=True)
-    o, fs, _, _ = pu.run_forward(inp, route=route, save_context=False)
+    ck = 64 if route == 3 else 0
+    o, fs, _, _ = pu.run_forward(inp, route=route, ckpt=ck, save_context=route == 3)
     ref_o, ref_s = pu.oracle_forward(inp)
     o = o.float().cpu().numpy()
     fs = fs.cpu().numpy()
@@ -60,16 +71,57 @@ def test_forward_edge(case, route):
         # nothing ever enters the state: both outputs are exactly zero
         assert np.all(o == 0.0) and np.all(fs == 0.0)
     pu.assert_close("o", o, ref_o)
-    print(f"  final-state max-abs error {np.abs(fs - ref_s).max():.3g}", flush=True)
-    if case == "no_decay" and route == 1:
-        # Without decay nothing forgets the rounding of the chunk route's BF16
-        # intra-chunk products (Akk, Kg S0^T), so its final-state error grows
-        # with length (about 6e-3 at 300 tokens for |S| up to 2.5) instead of
-        # staying near 5e-5 as under the configs' gates; this case is held to
-        # the pages' own bar.  The FP32 row-split route meets 1e-3.
-        pu.assert_close("final_state", fs, ref_s)
-    else:
-        pu.assert_state_close("final_state", fs, ref_s)
+    mx = pu.assert_state_close("final_state", fs, ref_s)
+    print(f"  final-state max-abs error {mx:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("case", ["no_decay", "no_decay_1024"])
+def test_fast_precision_drifts_without_decay(case):
+    """What the precise chunks are for: forced off (KDA_PRECISION_FAST), the
+    chunked route's final state drifts past the 1e-3 bar when nothing decays,
+    while every chunk forced precise (FULL) matches the automatic choice's
+    accuracy."""
+    import gated_delta_rule_32_amd as kda
+    problem, seed, set_to = CASES[case]
+    inp = _inputs(problem, seed, **set_to)
+    d = inp.to("cuda")
+    ref_o, ref_s = pu.oracle_forward(inp)
+    errs = {}
+    for prec in (kda.PRECISION_FAST, kda.PRECISION_FULL, kda.PRECISION_AUTO):
+        o, fs, _ = kda.recurrent_kda_training_forward(
+            d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
+            cu_seqlens=d.cu_seqlens, cu_seqlens_cpu=inp.cu_seqlens, route=kda.ROUTE_CHUNK,
+            save_context=False, precision=prec)
+        torch.cuda.synchronize()
+        pu.assert_close("o", o.float().cpu().numpy(), ref_o)
+        errs[prec] = float(np.abs(fs.cpu().numpy() - ref_s).max())
+    print(f"  final-state max-abs: fast {errs[kda.PRECISION_FAST]:.3g} "
+          f"full {errs[kda.PRECISION_FULL]:.3g} auto {errs[kda.PRECISION_AUTO]:.3g}", flush=True)
+    assert errs[kda.PRECISION_FAST] > pu.STATE_ATOL
+    assert errs[kda.PRECISION_FULL] <= pu.STATE_ATOL and errs[kda.PRECISION_AUTO] <= pu.STATE_ATOL
+
+
+@pytest.mark.parametrize("name", ["packed", "mixed"])
+def test_full_precision_on_workload(name):
+    """Every chunk forced precise on a benchmark workload (sampled tasks):
+    the precise path itself at full size, not only where weak decay picks it."""
+    import gated_delta_rule_32_amd as kda
+    inp = workloads.make_workload(name, with_adjoints=False)
+    problem = inp.problem
+    d = inp.to("cuda")
+    tasks = [(0, 0), (problem.N // 2, problem.Hv // 2), (problem.N - 1, problem.Hv - 1)]
+    print(f"[edge] precision FULL on {name}, tasks {tasks}", flush=True)
+    o, fs, _ = kda.recurrent_kda_training_forward(
+        d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
+        cu_seqlens=d.cu_seqlens, cu_seqlens_cpu=inp.cu_seqlens, save_context=True,
+        precision=kda.PRECISION_FULL)
+    torch.cuda.synchronize()
+    ref_o, ref_s = pu.oracle_forward(inp, tasks=tasks)
+    m = pu.task_mask_tokens(problem, tasks)
+    pu.report_and_check([("o", o.float().cpu().numpy()[m], ref_o[m])])
+    fs = fs.cpu().numpy()
+    for (n, h) in tasks:
+        pu.assert_state_close(f"final_state[{n},{h}]", fs[n, h], ref_s[n, h])
 
 
 @pytest.mark.parametrize("route", [1, 2], ids=["fwd-chunk", "fwd-rowsplit"])

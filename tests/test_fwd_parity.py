@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from tests import parity_util as pu
 
@@ -67,6 +68,56 @@ def test_forward_workloads_sampled(name, route):
     fs_np = fs.cpu().numpy()
     for (n, h) in tasks:
         pu.assert_state_close(f"final_state[{n},{h}]", fs_np[n, h], ref_s[n, h])
+    assert np.isfinite(o_np).all() and np.isfinite(fs_np).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "fixed", "grouped", "packed"])
+def test_forward_workloads_full_auto(name):
+    """Every task of the workload on the automatic route, with the context
+    saved (as in training and the benchmark, so the fixed 2x2048 workload runs
+    segment-parallel through its 256-token tape): o and every final state
+    against the oracle (page "flashinfer.kda_training", paragraph 6: the full
+    packed shape, all outputs)."""
+    import gated_delta_rule_32_amd as kda
+    inp = workloads.make_workload(name, with_adjoints=False)
+    problem = inp.problem
+    route = kda.kda_plan_query(kda.make_problem(problem.B, problem.T, problem.Hqk, problem.Hv,
+                                                problem.N, inp.cu_seqlens, inp.cu_seqlens))[0]
+    print(f"[fwd] workload={name} AUTO (route {route}), all {problem.N * problem.Hv} tasks",
+          flush=True)
+    o, fs, _, _ = pu.run_forward(inp, route=0, save_context=True)
+    o_np = o.float().cpu().numpy()
+    fs_np = fs.cpu().numpy()
+    del o, fs
+    ref_o, ref_s = pu.oracle_forward(inp, workers=oracle.default_workers())
+    pu.report_and_check([("o", o_np, ref_o)])
+    mx = pu.assert_state_close("final_state", fs_np, ref_s)
+    print(f"  final-state max-abs {mx:.3g} (ratio {mx / pu.STATE_ATOL:.3g})", flush=True)
+
+
+def _mixed_tasks_per_head(problem):
+    """One task per value head of the mixed workload, the heads walking over
+    the sequences in a stride-7 cycle of their longest-first order, so every
+    sequence appears twice and the tasks sit in all three dispatch rounds."""
+    order = sorted(range(problem.N), key=lambda n: -problem.lengths[n])
+    return [(order[(7 * h) % problem.N], h) for h in range(problem.Hv)]
+
+
+def test_forward_mixed_per_head_auto():
+    inp = workloads.make_workload("mixed", with_adjoints=False)
+    problem = inp.problem
+    tasks = _mixed_tasks_per_head(problem)
+    print(f"[fwd] workload=mixed AUTO, {len(tasks)} tasks (one per head)", flush=True)
+    o, fs, _, _ = pu.run_forward(inp, route=0, save_context=True)
+    o_np = o.float().cpu().numpy()
+    fs_np = fs.cpu().numpy()
+    del o, fs
+    ref_o, ref_s = pu.oracle_forward(inp, tasks=tasks, workers=oracle.default_workers())
+    m = pu.task_mask_tokens(problem, tasks)
+    pu.report_and_check([("o", o_np[m], ref_o[m])])
+    worst = max(pu.assert_state_close(f"final_state[{n},{h}]", fs_np[n, h], ref_s[n, h])
+                for (n, h) in tasks)
+    print(f"  final-state max-abs {worst:.3g} (ratio {worst / pu.STATE_ATOL:.3g})", flush=True)
     assert np.isfinite(o_np).all() and np.isfinite(fs_np).all()
 
 

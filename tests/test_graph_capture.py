@@ -1,7 +1,8 @@
 """kda_fwd and kda_bwd recorded into a HIP graph (torch.cuda.CUDAGraph) and
 replayed: every replay must reproduce the eager results bit for bit (the
 kernels are deterministic), with eager work and synchronisations between the
-replays.  A call under capture whose schedule is not cached yet must fail on
+replays, and every replay's o, final state and eight gradients must meet the
+method's bars against the FP64 oracle.  A call under capture whose schedule is not cached yet must fail on
 the host with KDA_ERR_CAPTURE and enqueue nothing.
 """
 import numpy as np
@@ -9,6 +10,7 @@ import pytest
 import torch
 
 import workloads
+from tests import parity_util as pu
 
 pytestmark = pytest.mark.gpu
 
@@ -75,6 +77,8 @@ def test_captured_step_replays_match_eager(case):
     with torch.cuda.graph(graph):
         step.run()
     torch.cuda.synchronize()
+    ref_o, ref_s = pu.oracle_forward(inp)
+    ref_g = pu.oracle_backward(inp)
     for rep in range(4):
         # eager work between replays: clobber every output, then replay
         for t in step.outputs():
@@ -85,6 +89,9 @@ def test_captured_step_replays_match_eager(case):
         got = _host(step.outputs())
         for i, (a, b) in enumerate(zip(got, eager)):
             assert np.array_equal(a, b), f"replay {rep}: output {i} differs from the eager result"
+        print(f"  replay {rep} against the oracle", flush=True)
+        pu.report_and_check([("o", got[0], ref_o)] + list(zip(pu.GRAD_NAMES, got[2:], ref_g)))
+        pu.assert_state_close(f"replay {rep} final_state", got[1], ref_s)
     # an eager call after the replays still matches as well
     step.run()
     torch.cuda.synchronize()
@@ -115,7 +122,10 @@ def test_captured_inference_replays_match_eager(route):
     in place, so it is restored before each replay)."""
     import gated_delta_rule_32_amd as kda
     problem = P([1, 9, 33, 16], 1, 2, packed=True)
-    inp = workloads.make_infer_inputs(problem, 404 + route, 6)
+    # the chunked route takes only the in-kernel gate (raw g, lower bound -5)
+    chunk = route == 1
+    inp = workloads.make_infer_inputs(problem, 404 + route, 6,
+                                      **(dict(log_gate_min=None) if chunk else {}))
     print(f"[graph] inference route={route}", flush=True)
     dev = torch.device("cuda")
     t = [x.to(dev) for x in (inp.q, inp.k, inp.v, inp.g, inp.beta)]
@@ -125,10 +135,13 @@ def test_captured_inference_replays_match_eager(route):
     o = torch.empty_like(t[2])
     prob = kda.make_infer_problem(1, problem.T, problem.Hqk, problem.Hv, problem.N, 6, cu,
                                   inp.cu_seqlens, state_indices=idx, state_indices_cpu=inp.indices,
-                                  route=route)
+                                  route=route, use_gate_in_kernel=chunk,
+                                  lower_bound=-5.0 if chunk else None)
+    A_log = inp.A_log.to(dev) if chunk else None
+    dt_bias = inp.dt_bias.to(dev) if chunk else None
 
     def run():
-        kda.kda_infer(prob, *t, None, None, pool, o, torch.cuda.current_stream().cuda_stream)
+        kda.kda_infer(prob, *t, A_log, dt_bias, pool, o, torch.cuda.current_stream().cuda_stream)
     for _ in range(2):                      # make the schedule, then see it settled
         pool.copy_(pool0)
         run()

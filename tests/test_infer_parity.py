@@ -53,10 +53,30 @@ def _binding_opts(opts):
     return out
 
 
-# cases whose log-decays can fall below -5 per token: token-serial route only
-TOKEN_ONLY = {"prefill_strong_log_gate"}
+# the chunked route takes only the in-kernel gate with lower_bound >= -5 (a
+# log-space gate has no bound the host can check): other cases run token by
+# token
+TOKEN_ONLY = {c for c, v in CASES.items() if not v[3].get("use_gate_in_kernel")}
 ROUTES = {"chunk": 1, "token": 2}
 PARAMS = [(c, r) for c in CASES for r in ROUTES if not (r == "chunk" and c in TOKEN_ONLY)]
+
+
+def _gate_gen(route):
+    """Input options for the tests below that run on either route: raw gate
+    inputs for the in-kernel gate on the chunked route (the only gate it
+    takes), the default log-space decays token by token."""
+    return dict(log_gate_min=None) if route == "chunk" else dict()
+
+
+def _gate_kw(route, inp, dev):
+    """The binding's and the oracle's gate arguments for _gate_gen's inputs:
+    the in-kernel gate with lower bound -5 on the chunked route, none (g is
+    the log-decay itself) token by token."""
+    if route != "chunk":
+        return dict(), dict(A_log=None, dt_bias=None)
+    opts = dict(use_gate_in_kernel=True, lower_bound=-5.0)
+    return (dict(A_log=inp.A_log.to(dev), dt_bias=inp.dt_bias.to(dev), **opts),
+            dict(A_log=inp.A_log, dt_bias=inp.dt_bias, **opts))
 
 
 def _run_case(name, route):
@@ -129,16 +149,17 @@ def test_infer_state_checkpoints(route, every):
     token j*E; rows past the last start are not touched."""
     import gated_delta_rule_32_amd as kda
     problem = P([5, 16, 17, 40, 100], 1, 2, packed=True)
-    inp = workloads.make_infer_inputs(problem, 507, 7)
+    inp = workloads.make_infer_inputs(problem, 507, 7, **_gate_gen(route))
     counts = [-(-L // every) for L in problem.lengths]
     starts_cpu = torch.tensor([0] + list(np.cumsum(counts)), dtype=torch.int64)
     print(f"[infer] checkpoints route={route} every={every} rows={int(starts_cpu[-1])}", flush=True)
     dev = torch.device("cuda")
+    gcall, gref = _gate_kw(route, inp, dev)
     rows = int(starts_cpu[-1]) + 2
     ck = torch.full((rows, problem.Hv, 128, 128), 7.0, dtype=torch.bfloat16, device=dev)
     pool = inp.pool.to(dev)
     o, _pool, ck_out = kda.recurrent_kda(
-        inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev),
+        inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev), **gcall,
         initial_state=pool, cu_seqlens=inp.cu_seqlens.to(dev), cu_seqlens_cpu=inp.cu_seqlens,
         ssm_state_indices=inp.indices.to(dev), ssm_state_indices_cpu=inp.indices,
         state_checkpoints=ck, checkpoint_cu_starts=starts_cpu.to(dev),
@@ -146,8 +167,8 @@ def test_infer_state_checkpoints(route, every):
     torch.cuda.synchronize()
     assert ck_out.data_ptr() == ck.data_ptr()
     o_ref, pool_ref, ck_ref = kio.infer_forward(
-        inp.q, inp.k, inp.v, inp.g, inp.beta, None, None, inp.pool, problem.lengths, True,
-        indices=inp.indices.tolist(), checkpoint_every=every)
+        inp.q, inp.k, inp.v, inp.g, inp.beta, pool=inp.pool, lengths=problem.lengths, packed=True,
+        indices=inp.indices.tolist(), checkpoint_every=every, **gref)
     got = ck.float().cpu().numpy()
     n_rows = int(starts_cpu[-1])
     pu.report_and_check([("o", o.float().cpu().numpy(), o_ref),
@@ -168,7 +189,7 @@ def test_infer_checkpoint_rows_out_of_range_are_skipped(route):
     import gated_delta_rule_32_amd as kda
     every = 16
     problem = P([5, 16, 40], 1, 2, packed=True)
-    inp = workloads.make_infer_inputs(problem, 517, 5)
+    inp = workloads.make_infer_inputs(problem, 517, 5, **_gate_gen(route))
     counts = [-(-L // every) for L in problem.lengths]
     starts_cpu = torch.tensor([0] + list(np.cumsum(counts)), dtype=torch.int64)
     bad = starts_cpu + 1000
@@ -180,7 +201,7 @@ def test_infer_checkpoint_rows_out_of_range_are_skipped(route):
     args = (inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev))
     kw = dict(cu_seqlens=inp.cu_seqlens.to(dev), cu_seqlens_cpu=inp.cu_seqlens,
               ssm_state_indices=inp.indices.to(dev), ssm_state_indices_cpu=inp.indices,
-              route=ROUTES[route])
+              route=ROUTES[route], **_gate_kw(route, inp, dev)[0])
     pool_a, pool_b = inp.pool.to(dev), inp.pool.to(dev)
     o_a, _, _ = kda.recurrent_kda(*args, initial_state=pool_a, state_checkpoints=ck,
                                   checkpoint_cu_starts=bad.to(dev), checkpoint_cu_starts_cpu=starts_cpu,
@@ -235,23 +256,24 @@ def test_infer_source_pool(route):
     allowed), final states land in the state pool, the source is untouched."""
     import gated_delta_rule_32_amd as kda
     problem = P([3, 40, 17, 64], 1, 2, packed=True)
-    inp = workloads.make_infer_inputs(problem, 510, 6)
+    inp = workloads.make_infer_inputs(problem, 510, 6, **_gate_gen(route))
     gen = torch.Generator().manual_seed(511)
     src_cpu = (0.1 * torch.randn((3, problem.Hv, 128, 128), generator=gen)).to(torch.bfloat16)
     sidx_cpu = torch.tensor([2, 0, 2, 1], dtype=torch.int32)
     print(f"[infer] source pool route={route}", flush=True)
     dev = torch.device("cuda")
+    gcall, gref = _gate_kw(route, inp, dev)
     pool, src = inp.pool.to(dev), src_cpu.to(dev)
     o, _ = kda.recurrent_kda(
-        inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev),
+        inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev), **gcall,
         initial_state=pool, cu_seqlens=inp.cu_seqlens.to(dev), cu_seqlens_cpu=inp.cu_seqlens,
         ssm_state_indices=inp.indices.to(dev), ssm_state_indices_cpu=inp.indices,
         initial_state_source=src, initial_state_indices=sidx_cpu.to(dev),
         initial_state_indices_cpu=sidx_cpu, route=ROUTES[route])
     torch.cuda.synchronize()
     o_ref, pool_ref = kio.infer_forward(
-        inp.q, inp.k, inp.v, inp.g, inp.beta, None, None, inp.pool, problem.lengths, True,
-        indices=inp.indices.tolist(), source=src_cpu, source_indices=sidx_cpu.tolist())
+        inp.q, inp.k, inp.v, inp.g, inp.beta, pool=inp.pool, lengths=problem.lengths, packed=True,
+        indices=inp.indices.tolist(), source=src_cpu, source_indices=sidx_cpu.tolist(), **gref)
     named = inp.indices.tolist()
     got = pool.float().cpu().numpy()
     pu.report_and_check([("o", o.float().cpu().numpy(), o_ref),
@@ -339,15 +361,16 @@ def test_infer_long_single_sequence(route):
     """One 4096-token sequence (one task per head) on either route."""
     import gated_delta_rule_32_amd as kda
     problem = P([4096], 1, 2, packed=True)
-    inp = workloads.make_infer_inputs(problem, 513, 1)
+    inp = workloads.make_infer_inputs(problem, 513, 1, **_gate_gen(route))
     print(f"[infer] 4096-token sequence route={route}", flush=True)
     dev = torch.device("cuda")
+    gcall, gref = _gate_kw(route, inp, dev)
     pool = inp.pool.to(dev)
     o, _ = kda.recurrent_kda(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev),
                              inp.beta.to(dev), initial_state=pool, cu_seqlens=inp.cu_seqlens.to(dev),
-                             cu_seqlens_cpu=inp.cu_seqlens, route=ROUTES[route])
+                             cu_seqlens_cpu=inp.cu_seqlens, route=ROUTES[route], **gcall)
     torch.cuda.synchronize()
-    o_ref, pool_ref = kio.infer_forward(inp.q, inp.k, inp.v, inp.g, inp.beta, None, None, inp.pool,
-                                        problem.lengths, True)
+    o_ref, pool_ref = kio.infer_forward(inp.q, inp.k, inp.v, inp.g, inp.beta, pool=inp.pool,
+                                        lengths=problem.lengths, packed=True, **gref)
     pu.report_and_check([("o", o.float().cpu().numpy(), o_ref),
                          ("state_pool", pool.float().cpu().numpy(), pool_ref)])

@@ -163,6 +163,34 @@ def _make_from_gen(problem: Problem, gen, with_adjoints: bool) -> Inputs:
     return Inputs(problem, q, k, v, g, beta, A_log, dt_bias, s0, problem.cu_seqlens(), do, dfs)
 
 
+def make_inputs_on_device(problem: Problem, seed: int, device, with_adjoints: bool = True) -> Inputs:
+    """The same recipe drawn by a generator on `device` (fast for large
+    benchmark shapes; the values differ from the CPU draws of the same seed,
+    the distributions do not).  Used for timing only, never for parity."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    B, T, Hqk, Hv, N = problem.B, problem.T, problem.Hqk, problem.Hv, problem.N
+
+    def rn(shape):
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+
+    q = rn((B, T, Hqk, DIM)).to(torch.bfloat16)
+    k = rn((B, T, Hqk, DIM)).to(torch.bfloat16)
+    v = rn((B, T, Hv, DIM)).to(torch.bfloat16)
+    g = rn((B, T, Hv, DIM)).to(torch.bfloat16)
+    beta = rn((B, T, Hv)).to(torch.bfloat16)
+    A_log = 2.0 * torch.rand((Hv,), generator=gen, device=device, dtype=torch.float32)
+    dt_bias = 0.1 * rn((Hv, DIM))
+    s0 = torch.zeros((N, Hv, DIM, DIM), dtype=torch.float32, device=device) if problem.zero_state \
+        else 0.01 * rn((N, Hv, DIM, DIM))
+    do = dfs = None
+    if with_adjoints:
+        do = rn((B, T, Hv, DIM)).to(torch.bfloat16)
+        dfs = 0.01 * rn((N, Hv, DIM, DIM))
+    cu = problem.cu_seqlens()
+    return Inputs(problem, q, k, v, g, beta, A_log, dt_bias, s0,
+                  None if cu is None else cu.to(device), do, dfs, {"cu_seqlens_cpu": cu})
+
+
 def sequence_slices(problem: Problem):
     """(n, b, t0, L): sequence n lives in batch row b at tokens [t0, t0+L)."""
     out = []
