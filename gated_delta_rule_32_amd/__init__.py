@@ -90,6 +90,8 @@ _lib.kda_plan_query.argtypes = [_P, ctypes.POINTER(ctypes.c_int32),
                                 ctypes.POINTER(ctypes.c_int64), _vp, ctypes.c_int64]
 _lib.kda_fwd.restype = ctypes.c_int
 _lib.kda_fwd.argtypes = [_P] + [_vp] * 10 + [_vp, ctypes.c_size_t, _vp]
+_lib.kda_fwd_noalloc.restype = ctypes.c_int
+_lib.kda_fwd_noalloc.argtypes = [_P] + [_vp] * 10 + [_vp, ctypes.c_size_t, _vp]
 _lib.kda_bwd.restype = ctypes.c_int
 _lib.kda_bwd.argtypes = ([_P] + [_vp] * 8 + [_vp, ctypes.c_size_t] + [_vp] * 2 + [_vp] * 8
                          + [_vp, ctypes.c_size_t, _vp])
@@ -98,7 +100,9 @@ _lib.kda_infer.restype = ctypes.c_int
 _lib.kda_infer.argtypes = [ctypes.POINTER(KdaInferProblem)] + [_vp] * 10
 
 EXPORTED = ("kda_version", "kda_status_string", "kda_last_error", "kda_fwd_ctx_bytes",
-            "kda_bwd_workspace_bytes", "kda_plan_query", "kda_fwd", "kda_bwd", "kda_infer")
+            "kda_bwd_workspace_bytes", "kda_plan_query", "kda_fwd", "kda_bwd", "kda_infer",
+            "kda_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 4 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
 
 class KdaError(RuntimeError):
@@ -198,6 +202,18 @@ def kda_fwd(p: KdaProblem, q, k, v, g, beta, A_log, dt_bias, initial_state, o, f
     _check(_lib.kda_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                         _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(o),
                         _ptr(final_state), _ptr(ctx), ctx_bytes, stream))
+
+
+def kda_fwd_noalloc(p: KdaProblem, q, k, v, g, beta, A_log, dt_bias, initial_state, o,
+                    final_state, ctx: Optional[torch.Tensor], stream: Optional[int] = None) -> None:
+    """C kda_fwd_noalloc (the schedule in the library's static device scratch;
+    no device allocation) on torch tensors."""
+    if stream is None:
+        stream = _stream_handle(q.device)
+    ctx_bytes = 0 if ctx is None else ctx.numel() * ctx.element_size()
+    _check(_lib.kda_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                _ptr(A_log), _ptr(dt_bias), _ptr(initial_state), _ptr(o),
+                                _ptr(final_state), _ptr(ctx), ctx_bytes, stream))
 
 
 def kda_bwd(p: KdaProblem, q, k, v, g, beta, A_log, dt_bias, initial_state, ctx, d_o,

@@ -34,6 +34,7 @@ SOURCES = [
     "kda_fwd_chunk.hip",
     "kda_bwd.hip",
     "kda_infer.hip",
+    "kda_noalloc.hip",
 ]
 
 FLAGS = [

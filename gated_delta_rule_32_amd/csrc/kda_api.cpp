@@ -711,6 +711,34 @@ kda_status kda_fwd(const kda_problem* pp, const void* q, const void* k, const vo
                       initial_state, o, final_state, ctx, ctx_bytes, stream);
 }
 
+kda_status kda_fwd_noalloc(const kda_problem* pp, const void* q, const void* k, const void* v,
+                           const void* g, const void* beta, const float* A_log,
+                           const float* dt_bias, const float* initial_state, void* o,
+                           float* final_state, void* ctx, size_t ctx_bytes, void* stream_) {
+    Prob p;
+    kda_status s = fwd_check(pp, p, q, k, v, g, beta, A_log, dt_bias, initial_state, o, final_state,
+                             ctx, ctx_bytes);
+    if (s != KDA_OK) return s;
+    const PlanLayout lay = plan_layout(p);
+    if (lay.bytes > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+        return fail(KDA_ERR_WORKSPACE_SIZE,
+                    "the schedule needs %zu bytes; the static scratch holds %zu "
+                    "(use kda_fwd for this problem)", lay.bytes, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+    hipStream_t stream = (hipStream_t)stream_;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    void* scratch = nullptr;
+    e = kda::noalloc_scratch(dev, &scratch);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    std::vector<char> host(lay.bytes);
+    fill_plan(p, lay, host.data());
+    e = kda::upload_to_scratch(scratch, host.data(), lay.bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "schedule upload launch");
+    return fwd_launch(p, dev, scratch, lay, q, k, v, g, beta, A_log, dt_bias, initial_state, o,
+                      final_state, ctx, ctx_bytes, stream);
+}
+
 kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const void* v,
                    const void* g, const void* beta, const float* A_log, const float* dt_bias,
                    const float* initial_state, const void* ctx, size_t ctx_bytes,

@@ -113,4 +113,11 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_reduce(const BwdArgs& a, int N, hipStream_t s);
 hipError_t launch_bwd_segments(const BwdArgs& a, int N, hipStream_t s);
 
+// The static device scratch of kda_fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES per
+// device): its address on device `dev` (found once per device, with `dev`
+// current), and a stream-ordered copy of `bytes` (a multiple of 4) of host
+// data into it by kernel launches that carry the data as arguments.
+hipError_t noalloc_scratch(int dev, void** ptr);
+hipError_t upload_to_scratch(void* scratch, const void* host, size_t bytes, hipStream_t s);
+
 }  // namespace kda

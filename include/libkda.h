@@ -75,6 +75,8 @@ extern "C" {
 
 #define KDA_HEAD_DIM 128
 #define KDA_VERSION 1
+/* Size of the static device scratch of kda_fwd_noalloc (per device). */
+#define KDA_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 typedef enum {
     KDA_OK = 0,
@@ -198,6 +200,25 @@ kda_status kda_fwd(const kda_problem* p,
                    const float* initial_state,
                    void* o, float* final_state,
                    void* ctx, size_t ctx_bytes, void* stream);
+
+/* kda_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, checks, kernels and results as kda_fwd, but the schedule (task
+ * order, sequence and tape offsets, segment list) goes into a static device
+ * array of KDA_NOALLOC_SCRATCH_BYTES per device instead of library-allocated
+ * memory, written by small kernel launches on `stream` (no hipMalloc, no
+ * pinned host memory, no memset).  A problem whose schedule needs more than
+ * that (about 900k (sequence, value head) tasks) is refused with
+ * KDA_ERR_WORKSPACE_SIZE before any device work.  Every call on a device
+ * shares that device's array and overwrites it: calls that overlap on one
+ * device (other streams or threads) race, so serialise them.  The context it
+ * fills is accepted by kda_bwd like kda_fwd's. */
+kda_status kda_fwd_noalloc(const kda_problem* p,
+                           const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const float* A_log, const float* dt_bias,
+                           const float* initial_state,
+                           void* o, float* final_state,
+                           void* ctx, size_t ctx_bytes, void* stream);
 
 /* Training backward (pages "flashinfer.kda_backward.recurrent_kda_backward"
  * and "flashinfer.kda_training", paragraph 5).  Takes the same problem and
