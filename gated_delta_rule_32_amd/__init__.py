@@ -36,6 +36,7 @@ KDA_ERR_CAPTURE = 13
 ROUTE_AUTO, ROUTE_CHUNK, ROUTE_ROWSPLIT, ROUTE_SEGMENTS = 0, 1, 2, 3
 CONTEXT_TAPE, CONTEXT_RECORDS = 0, 1
 PRECISION_AUTO, PRECISION_FULL, PRECISION_FAST = 0, 1, 2
+SCHEDULE_LONGEST_FIRST, SCHEDULE_SEQUENCE = 0, 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -53,6 +54,7 @@ class KdaProblem(ctypes.Structure):
         ("scale", ctypes.c_float), ("lower_bound", ctypes.c_float),
         ("route", ctypes.c_int32), ("checkpoint_every", ctypes.c_int32),
         ("context", ctypes.c_int32), ("precision", ctypes.c_int32),
+        ("schedule", ctypes.c_int32),
     ]
 
 
@@ -147,7 +149,8 @@ def make_problem(B: int, T: int, Hqk: int, Hv: int, N: int,
                  cu_seqlens_cpu: Optional[torch.Tensor] = None,
                  scale: Optional[float] = None, lower_bound: float = -5.0,
                  route: int = ROUTE_AUTO, checkpoint_every: int = 0,
-                 context: int = CONTEXT_TAPE, precision: int = PRECISION_AUTO) -> KdaProblem:
+                 context: int = CONTEXT_TAPE, precision: int = PRECISION_AUTO,
+                 schedule: int = SCHEDULE_LONGEST_FIRST) -> KdaProblem:
     p = KdaProblem()
     p.B, p.T, p.Hqk, p.Hv, p.N = int(B), int(T), int(Hqk), int(Hv), int(N)
     p.cu_seqlens = _ptr(cu_seqlens)
@@ -158,6 +161,7 @@ def make_problem(B: int, T: int, Hqk: int, Hv: int, N: int,
     p.checkpoint_every = int(checkpoint_every)
     p.context = int(context)
     p.precision = int(precision)
+    p.schedule = int(schedule)
     # the struct holds raw pointers: keep the tensors alive with it
     p._keep = (cu_seqlens, cu_seqlens_cpu)
     return p

@@ -54,6 +54,7 @@ struct Prob {
     int ck;         // tape interval
     int ctxmode;    // KDA_CONTEXT_TAPE or KDA_CONTEXT_RECORDS
     int precision;  // kda_precision
+    int schedule;   // kda_schedule
     float scale;
     std::vector<int64_t> len;    // per sequence
     std::vector<int64_t> start;  // flattened token offset per sequence
@@ -114,6 +115,8 @@ kda_status validate(const kda_problem* p, Prob& out) {
         return fail(KDA_ERR_ROUTE, "per-chunk records need the chunked route");
     if (p->precision < KDA_PRECISION_AUTO || p->precision > KDA_PRECISION_FAST)
         return fail(KDA_ERR_ROUTE, "unknown precision %d", p->precision);
+    if (p->schedule != KDA_SCHEDULE_LONGEST_FIRST && p->schedule != KDA_SCHEDULE_SEQUENCE)
+        return fail(KDA_ERR_ROUTE, "unknown schedule %d", p->schedule);
 
     out = Prob{};
     out.B = p->B; out.T = p->T; out.Hqk = p->Hqk; out.Hv = p->Hv; out.N = p->N;
@@ -122,6 +125,7 @@ kda_status validate(const kda_problem* p, Prob& out) {
     out.ck = ck;
     out.ctxmode = p->context;
     out.precision = p->precision;
+    out.schedule = p->schedule;
     out.scale = want_scale;
     out.tokens = (int64_t)p->B * p->T;
     if (packed) {
@@ -167,11 +171,19 @@ kda_status validate(const kda_problem* p, Prob& out) {
 
 // Longest sequence first; ties keep sequence order.  Within a sequence the
 // value heads follow each other, so heads sharing a q/k head are adjacent.
-std::vector<int32_t> lpt_order(const Prob& p) {
+// Sequences in dispatch order: longest first (ties in sequence order), or
+// sequence order under KDA_SCHEDULE_SEQUENCE.
+std::vector<int> seq_order(const Prob& p) {
     std::vector<int> seqs(p.N);
     for (int n = 0; n < p.N; ++n) seqs[n] = n;
-    std::stable_sort(seqs.begin(), seqs.end(),
-                     [&](int a, int b) { return p.len[a] > p.len[b]; });
+    if (p.schedule == KDA_SCHEDULE_LONGEST_FIRST)
+        std::stable_sort(seqs.begin(), seqs.end(),
+                         [&](int a, int b) { return p.len[a] > p.len[b]; });
+    return seqs;
+}
+
+std::vector<int32_t> lpt_order(const Prob& p) {
+    const std::vector<int> seqs = seq_order(p);
     std::vector<int32_t> order;
     order.reserve((size_t)p.num_tasks);
     for (int n : seqs)
@@ -214,17 +226,14 @@ void fill_plan(const Prob& p, const PlanLayout& l, char* h) {
     to[0] = 0;
     co[0] = 0;
     int64_t si = 0;
-    // segments in longest-first order of their sequences
-    std::vector<int> seqs(p.N);
+    // segments in the dispatch order of their sequences
     for (int n = 0; n < p.N; ++n) {
-        seqs[n] = n;
         st[n] = p.start[n];
         ln[n] = (int32_t)p.len[n];
         to[n + 1] = to[n] + (p.len[n] + p.ck - 1) / p.ck - 1;
         co[n + 1] = co[n] + (p.len[n] + kChunk - 1) / kChunk;
     }
-    std::stable_sort(seqs.begin(), seqs.end(), [&](int a, int b) { return p.len[a] > p.len[b]; });
-    for (int n : seqs) {
+    for (int n : seq_order(p)) {
         const int64_t nseg = (p.len[n] + p.ck - 1) / p.ck;
         for (int64_t j = 0; j < nseg; ++j) {
             sg[2 * si] = n;
@@ -340,7 +349,7 @@ struct PlanLease {
 };
 
 std::vector<int64_t> plan_key(const Prob& p, int dev) {
-    std::vector<int64_t> key = {dev, p.Hv, p.ck, p.packed ? 1 : 0, p.T, p.N};
+    std::vector<int64_t> key = {dev, p.Hv, p.ck, p.packed ? 1 : 0, p.T, p.N, p.schedule};
     key.insert(key.end(), p.len.begin(), p.len.end());
     return key;
 }

@@ -94,6 +94,30 @@ __device__ __forceinline__ void split4(f32x4 x, bf16x4& hi, bf16x4& lo) {
     lo = to_bf4(x - h);
 }
 
+// FP16 pairs.  FP16 keeps 11 significant bits (BF16 8) in a narrower range
+// (|x| < 65504; below 6.1e-5 it loses bits, below 6e-8 it is zero), so it
+// serves operands whose magnitude is bounded and whose small values do not
+// matter.  hi = f16(x), lo = f16(x - hi) carry about 22 bits.
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {  // round to nearest even, pair by pair
+    const f16x2 a = __builtin_convertvector(f32x2{x[0], x[1]}, f16x2);
+    const f16x2 b = __builtin_convertvector(f32x2{x[2], x[3]}, f16x2);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3);
+}
+__device__ __forceinline__ void split4_f16(f32x4 x, f16x4& hi, f16x4& lo) {
+    hi = to_f16x4(x);
+    lo = to_f16x4(x - __builtin_convertvector(hi, f32x4));
+}
+__device__ __forceinline__ f16x8 cat8h(f16x4 a, f16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 mma32h(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // The same pair with hi rounded to nearest (unbiased, so that hi may also
 // serve alone as the operand's BF16 value): hi = bf16(x), lo = bf16(x - hi),
 // where x - hi is exact.

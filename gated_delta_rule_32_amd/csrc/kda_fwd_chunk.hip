@@ -34,13 +34,20 @@
 // O^T = S0 Qg^T + U^T Aqk^T, whose accumulator layout gives each lane four
 // consecutive channels of one token, stored straight to global memory.
 //
-// Precision.  Only the products that add new information to the carried state
-// need FP32-accurate operands: Tb V (Tb as a BF16 hi/lo pair, V exact) and
-// U^T Kt (both operands as hi/lo pairs, three products).  Kg S0^T, Tb Y, the A
-// matrices and the output use plain BF16 operands: the delta rule re-measures
-// the state against each key, so rounding in the prediction does not
-// accumulate (checked against the FP64 definition over 1024-4096-token
-// sequences: final-state error ~2e-5 to 5e-5).
+// Precision.  The products that write new information into the carried
+// state need FP32-like operands: Tb V (Tb as a BF16 hi/lo pair, V exact in
+// BF16) and U^T Kt, done in FP16 as [Kt_hi|Kt_lo] [U;U] in one 16x16x32 per
+// state frag (Kt lies in [0, 1] and keeps about 22 bits as an FP16 pair; U
+// keeps 11; U of 16384 or more is scaled by a power of two around the
+// product).  The products that predict the state (Kg S0^T, Tb Y, Akk) and the
+// output use single BF16 operands: under decay the delta rule re-measures the
+// state against each key and the prediction's rounding fades within a few
+// tokens (final-state error 5e-5 to 3e-4 against the FP64 definition over
+// 1024-4096 tokens for chunk decays up to exp(-2)).  A channel that decays
+// less keeps that rounding: a chunk in which some channel keeps more than
+// exp(-2) of its state ("precise") takes Kg, Ki, S0 and Y as BF16 hi/lo pairs
+// too (three products each) and U as an FP16 hi/lo pair, which holds the
+// final state within about 3e-5 without any decay.
 #include <type_traits>
 
 #include "kda_chunk.hpp"
@@ -72,10 +79,11 @@ struct FwdLds {
     alignas(16) bf16 rf_kg_lo[8 * FS];  // precise chunks: lo parts of Kg, Ki
     alignas(16) bf16 rf_ki_lo[8 * FS];
     alignas(16) bf16 cf_kt[8 * FS2];  // CF(Kt) as [hi | lo] pairs, 8 bf16 per lane
+    alignas(16) f16x4 ulo[4][2][64];  // precise chunks: each wave's FP16 lo part of U
     int precise[2];                   // by chunk parity: the chunk runs precise
 };
 
-struct ColIn {   // V for the wave's 32 columns: RF(V)[2w], RF(V)[2w+1]
+struct ColIn {   // V for the wave's 32 columns: CF(V)[2w], CF(V)[2w+1]
     bf16x4 v0, v1;
 };
 
@@ -99,10 +107,17 @@ __device__ __forceinline__ void load_rows_s(RowIn& x, const SeqPtrs& p, unsigned
     x.g = *(const bf16x8*)at(p.g, __umul24(t, p.sv) + c8);
     x.b = *at(p.beta, __umul24(t, p.sb));
 }
-__device__ __forceinline__ void load_cols_s(ColIn& x, const SeqPtrs& p, unsigned t, unsigned ch0) {
-    const unsigned o = __umul24(t, p.sv) + ch0;
-    x.v0 = *(const bf16x4*)at(p.v, o);
-    x.v1 = *(const bf16x4*)at(p.v, o + 16);
+// CF(V) straight from memory: lane (gq, n) takes tokens t4 .. t4+3 (t4 =
+// t0 + 4gq, each clamped to the sequence's last token, whose rows the
+// chunk's zero beta then masks) of channels ch and ch + 16: eight 2-byte
+// loads into the halves of four registers, no transpose.
+__device__ __forceinline__ void load_cols_cf(ColIn& x, const SeqPtrs& p, int t4, int last, unsigned ch) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned o = __umul24((unsigned)min(t4 + i, last), p.sv) + ch;
+        x.v0[i] = *at(p.v, o);
+        x.v1[i] = *at(p.v, o + 16);
+    }
 }
 
 __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], int wave, int gq,
@@ -257,7 +272,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     {
         const int lane = tid & 63;
         load_rows_s(cur, sp, min(cb * CH + (tid >> 4), L - 1), (tid & 15) * 8);
-        load_cols_s(vcur, sp, min(cb * CH + (lane & 15), L - 1), 32 * wave + 4 * (lane >> 4));
+        load_cols_cf(vcur, sp, cb * CH + 4 * (lane >> 4), L - 1, 32 * wave + (lane & 15));
     }
     __syncthreads();
 
@@ -387,8 +402,10 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         // and the backward's rebuild takes the same decisions as the forward,
         // so it reproduces the forward's chunk states exactly.
         const bool precise = __builtin_amdgcn_readfirstlane(sm.precise[ci & 1]) != 0;
-        // ---- C: decay factors and the chunk's operands ----
-        {
+        // ---- C: decay factors and the chunk's operands (one branch for the
+        // whole phase, so that each variant is scheduled on its own) ----
+        auto phase_c = [&](auto prec_tag) __attribute__((always_inline)) {
+            constexpr bool kPrecise = decltype(prec_tag)::value;
             float gc[8], gC[8];
             *(float4*)&gc[0] = *(const float4*)&sm.lam[r][c8];
             *(float4*)&gc[4] = *(const float4*)&sm.lam[r][c8 + 4];
@@ -411,7 +428,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                     kt[j] = ki[j] * gC[i];
                 }
                 qg4[s4] = to_bf4(qg);
-                if (precise) {
+                if constexpr (kPrecise) {
                     bf16x4 kl, il;
                     split4(kg, kg4[s4], kl);
                     split4(ki, ki4[s4], il);
@@ -422,7 +439,14 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                     kg4[s4] = to_bf4(kg);
                     ki4[s4] = to_bf4(ki);
                 }
-                split4(kt, th4[s4], tl4[s4]);
+                {
+                    // FP16 pair (about 22 bits): Kt lies in [0, 1]; what falls
+                    // below FP16's range is a contribution under 1e-7 of |U|
+                    f16x4 h, l;
+                    split4_f16(kt, h, l);
+                    th4[s4] = __builtin_bit_cast(bf16x4, h);
+                    tl4[s4] = __builtin_bit_cast(bf16x4, l);
+                }
             }
             const int orf = rf_off(r, c8);  // channels c8+4.. sit one lane group later
 #pragma unroll
@@ -431,9 +455,10 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 *(bf16x4*)&sm.rf_kg[orf + 64 * s] = kg4[s];
                 *(bf16x4*)&sm.rf_ki[orf + 64 * s] = ki4[s];
             }
-            // CF(Kt) hi / lo pairs: lane slot (gq, k) holds the hi parts of
-            // tokens 4gq..4gq+3, then their lo parts; channel c8 + j of row r
-            // sits 8j elements after channel c8 (one 16-channel block)
+            // CF(Kt) hi / lo pairs (BF16 in precise chunks, FP16 in the
+            // others): lane slot (gq, k) holds the hi parts of tokens
+            // 4gq..4gq+3, then their lo parts; channel c8 + j of row r sits 8j
+            // elements after channel c8 (one 16-channel block)
             const int ocf = (c8 >> 4) * FS2 + (((r >> 2) << 4) + (c8 & 15)) * 8 + (r & 3);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -442,7 +467,11 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 sm.cf_kt[ocf + 8 * j + 4] = tl4[0][j];
                 sm.cf_kt[ocf + 8 * (j + 4) + 4] = tl4[1][j];
             }
-        }
+        };
+        if (precise)
+            phase_c(std::true_type{});
+        else
+            phase_c(std::false_type{});
         // the row inputs are dead: fetch the next chunk's into the same registers
         load_rows_s(cur, sp, min(t0 + CH + r, L - 1), c8);
         __syncthreads();
@@ -522,16 +551,23 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         if (wave == 0) {
             SolveScratch& ws = sm.sv;
             f32x4 akk = zero4();
+            if (precise) {   // Kg_hi Ki_hi + Kg_hi Ki_lo + Kg_lo Ki_hi
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
-                const bf16x8 ki8 = cat8(ld4(&sm.rf_ki[(2 * j) * FS], lane), ld4(&sm.rf_ki[(2 * j + 1) * FS], lane));
-                akk = mma32(kg8, ki8, akk);     // lane (gq, c) holds Akk[4gq+i][c]
-                if (precise) {                  // + Kg_hi Ki_lo + Kg_lo Ki_hi
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
+                    const bf16x8 ki8 = cat8(ld4(&sm.rf_ki[(2 * j) * FS], lane), ld4(&sm.rf_ki[(2 * j + 1) * FS], lane));
+                    akk = mma32(kg8, ki8, akk);
                     akk = mma32(kg8, cat8(ld4(&sm.rf_ki_lo[(2 * j) * FS], lane),
                                           ld4(&sm.rf_ki_lo[(2 * j + 1) * FS], lane)), akk);
                     akk = mma32(cat8(ld4(&sm.rf_kg_lo[(2 * j) * FS], lane),
                                      ld4(&sm.rf_kg_lo[(2 * j + 1) * FS], lane)), ki8, akk);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
+                    const bf16x8 ki8 = cat8(ld4(&sm.rf_ki[(2 * j) * FS], lane), ld4(&sm.rf_ki[(2 * j + 1) * FS], lane));
+                    akk = mma32(kg8, ki8, akk);     // lane (gq, c) holds Akk[4gq+i][c]
                 }
             }
             y_ot();
@@ -619,22 +655,17 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         }
         bf16x8 aq2;
         if constexpr (kOut) aq2 = *(const bf16x8*)&sm.sh_aq[lane * 8];
-        // CF(V) for the wave's columns (RF(V) times the identity, exact), then
-        // U = Tb V - Tb Y
+        // U = Tb V - Tb Y (CF(V) loaded directly)
         f32x4 U[2];
         {
-            f32x4 id;  // lane (gq, n) holds I[4gq+i][n]
-#pragma unroll
-            for (int i = 0; i < 4; ++i) id[i] = (4 * gq + i == cl) ? 1.0f : 0.0f;
-            const bf16x4 ident = to_bf4(id);
             if constexpr (kSegPQ) {
                 if (!segQ) {  // P runs with v = 0
                     vcur.v0 = to_bf4(zero4());
                     vcur.v1 = to_bf4(zero4());
                 }
             }
-            const bf16x4 cfv0 = to_bf4(mma16(vcur.v0, ident, zero4()));
-            const bf16x4 cfv1 = to_bf4(mma16(vcur.v1, ident, zero4()));
+            const bf16x4 cfv0 = vcur.v0;
+            const bf16x4 cfv1 = vcur.v1;
             // a 16x16x32 costs about what a 16x16x16 does, so the hi/lo
             // products take two: [Tb_hi|Tb_lo] [V;V] and [Tb_hi|Tb_lo] [-Y;-Y]
             // (every operand tuple is formed where it is produced, no copies)
@@ -654,46 +685,100 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 U[1] = mma32(tb2, cat8(to_bf4_neg(Y[1]), to_bf4_neg(Y[1])), U[1]);
             }
         }
-        load_cols_s(vcur, sp, min(t0 + CH + cl, L - 1), 32 * wave + 4 * gq);
-        // O^T += U^T Aqk^T, store; then S update.  U as [hi|hi] and [lo|lo]
-        bf16x8 uu[2], ll[2];
-#pragma unroll
-        for (int vb = 0; vb < 2; ++vb) {
-            bf16x4 uh, ul;
-            split4(U[vb], uh, ul);
-            uu[vb] = cat8(uh, uh);
-            ll[vb] = cat8(ul, ul);
+        load_cols_cf(vcur, sp, t0 + CH + 4 * gq, L - 1, 32 * wave + cl);
+        // O^T += U^T Aqk^T, store; then the state update S^T += Kt^T U
+        auto out_term = [&](int vb, bf16x4 uh) __attribute__((always_inline)) {
             if constexpr (kRec) {
                 // U record, RF layout: lane (gq, c) holds U[c][16vb + 4gq + i]
                 const bf16x4 ut = to_bf4(transpose_frag(to_bf4(U[vb]), identity_frag(lane)));
                 *(bf16x4*)at((bf16*)a.rec_u + rec * (CH * D), ((2 * wave + vb) * 64 + lane) * 4) = ut;
             }
-            if constexpr (!kOut) continue;
-            // the chain's last step is a 16x16x32 as well
-            OT[vb] = mma32(uu[vb], aq2, OT[vb]);
-            // lane (gq, c) holds O[c][32w + 16vb + 4gq + i]
-            if (cl < nv) {
-                const bf16x4 ob = to_bf4(OT[vb]);
-                *(bf16x4*)at(sp.o, __umul24((unsigned)(t0 + cl), sp.sv) + 32 * wave + 16 * vb + 4 * gq) = ob;
+            if constexpr (kOut) {
+                // [U_hi|U_hi] against [Aqk/2;Aqk/2]: the chain's last step is a
+                // 16x16x32 as well; lane (gq, c) holds O[c][32w + 16vb + 4gq + i]
+                OT[vb] = mma32(cat8(uh, uh), aq2, OT[vb]);
+                if (cl < nv) {
+                    const bf16x4 ob = to_bf4(OT[vb]);
+                    *(bf16x4*)at(sp.o, __umul24((unsigned)(t0 + cl), sp.sv) + 32 * wave + 16 * vb + 4 * gq) = ob;
+                }
             }
-        }
+        };
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb) out_term(vb, to_bf4(U[vb]));
         phase_b(ci + 1);
-        // S^T += Kt^T U as [Kt_hi|Kt_lo] [U_hi;U_hi] + [Kt_hi|Kt_lo] [U_lo;U_lo]:
-        // all four hi/lo products in two 16x16x32s.  (One accumulation chain
-        // keeps one MFMA shape: a 16x16x16 that reads the accumulator of a
-        // 16x16x32 issued just before it has been seen to miss that product.)
+        // S^T += Kt^T U in FP16, [Kt_hi|Kt_lo] (about 22 bits) against [U;U]
+        // (11 bits) in one 16x16x32 per state frag; precise chunks add
+        // [Kt_hi|Kt_lo] [U_lo;U_lo] (U to about 22 bits as well).  (One
+        // accumulation chain keeps one MFMA shape: a 16x16x16 that reads the
+        // accumulator of a 16x16x32 issued just before it has been seen to
+        // miss that product.)
+        // U beyond FP16's range (|U| of 16384 or more somewhere in the wave,
+        // or not finite) is scaled by 2^-e for the product, and the state
+        // with it (powers of two: exact), and both are scaled back after.
+        float um = 0.f;
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb)
+            um = fmaxf(um, fmaxf(fmaxf(fabsf(U[vb][0]), fabsf(U[vb][1])),
+                                 fmaxf(fabsf(U[vb][2]), fabsf(U[vb][3]))));
+        const bool big = __builtin_amdgcn_ballot_w64(!(um < 16384.f)) != 0;
+        float isc = 1.f;
+        if (big) {
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) um = fmaxf(um, __shfl_xor(um, o, 64));
+            const int e = __builtin_amdgcn_readfirstlane(um < 3.0e38f ? max(ilogbf(um) - 12, 0) : 116);
+            const float sc = ldexpf(1.f, -e);
+            isc = ldexpf(1.f, e);
+#pragma unroll
+            for (int vb = 0; vb < 2; ++vb) U[vb] *= sc;
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) S[kb][vb] *= sc;
+        }
+        // (a precise chunk parks U's lo part in LDS over the main loop, which
+        // then holds no value that only precise chunks need)
+        f16x8 uh8[2];
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb) {
+            f16x4 h, l;
+            if (precise) {
+                split4_f16(U[vb], h, l);
+                sm.ulo[wave][vb][lane] = l;
+            } else {
+                h = to_f16x4(U[vb]);
+            }
+            uh8[vb] = cat8h(h, h);
+        }
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-            const bf16x8 t2 = *(const bf16x8*)&sm.cf_kt[kb * FS2 + lane * 8];
+            const f16x8 t2 = *(const f16x8*)&sm.cf_kt[kb * FS2 + lane * 8];
             const float4 gd = *(const float4*)&sm.gamc[ci & 1][16 * kb + 4 * gq];
 #pragma unroll
             for (int vb = 0; vb < 2; ++vb) {
                 f32x4 s = S[kb][vb];
                 s[0] *= gd.x; s[1] *= gd.y; s[2] *= gd.z; s[3] *= gd.w;
-                s = mma32(t2, uu[vb], s);
-                s = mma32(t2, ll[vb], s);
-                S[kb][vb] = s;
+                S[kb][vb] = mma32h(t2, uh8[vb], s);
             }
+        }
+        if (precise) {   // + [Kt_hi|Kt_lo] [U_lo;U_lo]
+            f16x8 ul8[2];
+#pragma unroll
+            for (int vb = 0; vb < 2; ++vb) {
+                const f16x4 l = sm.ulo[wave][vb][lane];
+                ul8[vb] = cat8h(l, l);
+            }
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                const f16x8 t2 = *(const f16x8*)&sm.cf_kt[kb * FS2 + lane * 8];
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) S[kb][vb] = mma32h(t2, ul8[vb], S[kb][vb]);
+            }
+        }
+        if (big) {
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                for (int vb = 0; vb < 2; ++vb) S[kb][vb] *= isc;
         }
         const int tend = t0 + nv;
         if (kMode == kFwdTape && a.tape != nullptr && tend < L && (tend % a.ck_every) == 0) {

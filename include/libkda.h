@@ -144,6 +144,16 @@ typedef enum {
     KDA_PRECISION_FAST = 2
 } kda_precision;
 
+/* Order in which the (sequence, value head) tasks are dispatched.  Each task
+ * is owned by one workgroup, so the results do not depend on it.
+ * LONGEST_FIRST: longest sequence first (page "flashinfer.kda.recurrent_kda",
+ * parameter cu_seqlens), so that a long task does not start last and run
+ * alone; SEQUENCE: sequence order (for measuring what longest-first buys). */
+typedef enum {
+    KDA_SCHEDULE_LONGEST_FIRST = 0,
+    KDA_SCHEDULE_SEQUENCE = 1
+} kda_schedule;
+
 /* One call's shape.  All fields are read by value; the struct is not kept. */
 typedef struct {
     int32_t B;                       /* physical batch (1 when packed) */
@@ -159,6 +169,7 @@ typedef struct {
     int32_t checkpoint_every;        /* tape interval in tokens; 0 selects 256; a multiple of 16 */
     int32_t context;                 /* kda_context: what the forward saves for the backward */
     int32_t precision;               /* kda_precision; AUTO unless testing */
+    int32_t schedule;                /* kda_schedule; LONGEST_FIRST unless measuring */
 } kda_problem;
 
 /* Library version (KDA_VERSION). */

@@ -117,6 +117,11 @@ def test_longest_first_order():
     seqs = [o // 2 for o in order]
     assert [lens[s] for s in seqs] == sorted([lens[s] for s in seqs], reverse=True)
     assert order == [6, 7, 2, 3, 0, 1, 4, 5]
+    # sequence order on request (for measuring what longest-first buys)
+    p.schedule = kda.SCHEDULE_SEQUENCE
+    assert kda.kda_plan_query(p, with_order=True)[2] == list(range(8))
+    p.schedule = 2
+    assert _status(kda.kda_fwd_ctx_bytes, p) == 11
 
 
 def test_route_choice():

@@ -149,3 +149,27 @@ def test_long_single_sequence(route):
     got = pu.run_backward(inp, route=route)
     ref = pu.oracle_backward(inp)
     pu.report_and_check(list(zip(pu.GRAD_NAMES, got, ref)))
+
+
+@pytest.mark.parametrize("route", [1, 3], ids=["chunk", "segments"])
+def test_forward_huge_values(route):
+    """Values of order 1e5: U leaves FP16's range, so the plain chunks' FP16
+    state update scales U (and the state with it) by a power of two for the
+    product.  o and the final state are linear in (v, initial state), and v
+    dominates here, so both are compared after dividing by the value scale
+    2e5: the pages' bar (atol = rtol = 1e-2) on the scaled quantities, and the
+    scaled final state within 1e-3 (FP32 resolves about 0.01 at 1e5)."""
+    problem = P([64, 37], 1, 2, packed=True)
+    inp = workloads.make_inputs(problem, 213, with_adjoints=False)
+    inp.v = (inp.v.float() * 2.0e5).to(torch.bfloat16)
+    print(f"[edge fwd] huge values route={route}", flush=True)
+    o, fs, _, _ = pu.run_forward(inp, route=route, ckpt=32 if route == 3 else 0,
+                                 save_context=route == 3)
+    ref_o, ref_s = pu.oracle_forward(inp)
+    o = o.float().cpu().numpy()
+    fs = fs.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(fs).all()
+    print(f"  max |o| {np.abs(ref_o).max():.3g}, max |S| {np.abs(ref_s).max():.3g}", flush=True)
+    sc = 2.0e5
+    pu.report_and_check([("o", o / sc, ref_o / sc)])
+    pu.assert_state_close("final_state / 2e5", fs / sc, ref_s / sc)
