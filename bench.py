@@ -318,6 +318,8 @@ def main():
         out["fwd_cache_cold"] = cache_cold_forward(kda, prob, p, d, args, stream, flush)
         del flush
         out["cold_plan"] = cold_plan_call(kda, p, d, inp_cpu, stream)
+        if route in (0, 1):
+            out["precision_cost"] = precision_cost(kda, p, d, inp_cpu, args, stream)
     if p.name == "packed" and not args.no_extra:
         out["inference"] = inference_steps(kda, p, d, inp_cpu, args, stream)
         out["other_workloads"] = other_workloads(kda, args, stream)
@@ -381,6 +383,23 @@ def cache_cold_forward(kda, prob, p, d, args, stream, flush):
     gbs = algorithmic_fwd_bytes(p) / (f * 1e-3) / 1e9
     return {"ms_mean": round(f, 4), "flush_mb": args.flush_mb,
             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def precision_cost(kda, p, d, inp_cpu, args, stream):
+    """Forward and backward of the headline step under each precision mode:
+    the automatic choice (hi/lo operands only in chunks where some channel
+    keeps more than e^-2 of its state), never (single BF16 predictions), and
+    every chunk.  The automatic mode's cost over "fast" is the price of its
+    per-chunk check on this workload; "full" is the price of hi/lo operands
+    everywhere."""
+    res = {}
+    for name, mode in (("auto", kda.PRECISION_AUTO), ("fast", kda.PRECISION_FAST),
+                       ("full", kda.PRECISION_FULL)):
+        prob = kda.make_problem(p.B, p.T, p.Hqk, p.Hv, p.N, d.cu_seqlens, inp_cpu.cu_seqlens,
+                                route=args.route, precision=mode)
+        f, b = _fwd_bwd_times(kda, prob, d, stream, args.steps, args.warmup)
+        res[name] = {"fwd_ms_mean": round(f, 4), "bwd_ms_mean": round(b, 4)}
+    return res
 
 
 def cold_plan_call(kda, p, d, inp_cpu, stream):
