@@ -133,11 +133,11 @@ typedef enum {
  * whose decay is weak keeps it, and the FP32 state drifts past 1e-3.  AUTO
  * runs a chunk with BF16 hi/lo pairs on those operands too (three products
  * each, FP32-accurate) when some channel keeps more than exp(-2) of its state
- * over the chunk (the accurate full-precision-state recurrence of page
- * "flashinfer.kda_training", paragraph 5, here per chunk and only where the
- * decay makes it matter); FULL runs every chunk that way; FAST none (final
- * states can then miss 1e-3 on weakly decaying inputs).  The row-split route
- * is FP32 throughout and ignores this. */
+ * over the chunk (page "flashinfer.kda_training", paragraph 1: the chunked
+ * routes' public final state comes from a recurrence kept in full precision;
+ * here per chunk, and only where the decay makes it matter); FULL runs every
+ * chunk that way; FAST none (final states can then miss 1e-3 on weakly
+ * decaying inputs).  The row-split route is FP32 throughout and ignores this. */
 typedef enum {
     KDA_PRECISION_AUTO = 0,
     KDA_PRECISION_FULL = 1,
