@@ -33,7 +33,7 @@ SCALE = 1.0 / math.sqrt(128.0)
 KDA_OK = 0
 KDA_ERR_HIP = 12
 KDA_ERR_CAPTURE = 13
-ROUTE_AUTO, ROUTE_CHUNK, ROUTE_ROWSPLIT, ROUTE_SEGMENTS = 0, 1, 2, 3
+ROUTE_AUTO, ROUTE_CHUNK, ROUTE_ROWSPLIT, ROUTE_SEGMENTS, ROUTE_CHUNK_SPLIT = 0, 1, 2, 3, 4
 CONTEXT_TAPE, CONTEXT_RECORDS = 0, 1
 PRECISION_AUTO, PRECISION_FULL, PRECISION_FAST = 0, 1, 2
 SCHEDULE_LONGEST_FIRST, SCHEDULE_SEQUENCE = 0, 1

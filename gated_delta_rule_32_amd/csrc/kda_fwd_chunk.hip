@@ -83,8 +83,8 @@ struct FwdLds {
     int precise[2];                   // by chunk parity: the chunk runs precise
 };
 
-struct ColIn {   // V for the wave's 32 columns: CF(V)[2w], CF(V)[2w+1]
-    bf16x4 v0, v1;
+struct ColIn {   // V for the wave's 16-column blocks: CF(V)[vb0], CF(V)[vb0+1]
+    bf16x4 v[2];
 };
 
 // Per-task base pointers (uniform, so they live in scalar registers) and
@@ -109,24 +109,26 @@ __device__ __forceinline__ void load_rows_s(RowIn& x, const SeqPtrs& p, unsigned
 }
 // CF(V) straight from memory: lane (gq, n) takes tokens t4 .. t4+3 (t4 =
 // t0 + 4gq, each clamped to the sequence's last token, whose rows the
-// chunk's zero beta then masks) of channels ch and ch + 16: eight 2-byte
-// loads into the halves of four registers, no transpose.
+// chunk's zero beta then masks) of channels ch, ch + 16, ...: 2-byte loads
+// into the halves of four registers per block, no transpose.
+template <int NVB>
 __device__ __forceinline__ void load_cols_cf(ColIn& x, const SeqPtrs& p, int t4, int last, unsigned ch) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const unsigned o = __umul24((unsigned)min(t4 + i, last), p.sv) + ch;
-        x.v0[i] = *at(p.v, o);
-        x.v1[i] = *at(p.v, o + 16);
+#pragma unroll
+        for (int j = 0; j < NVB; ++j) x.v[j][i] = *at(p.v, o + 16 * j);
     }
 }
 
-__device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], int wave, int gq,
+template <int NVB>
+__device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][NVB], int vb0, int gq,
                                             int cl) {
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int vcol = 16 * (2 * wave + j) + cl;
+        for (int j = 0; j < NVB; ++j) {
+            const int vcol = 16 * (vb0 + j) + cl;
             *(float4*)(dst + (int64_t)vcol * D + 16 * kb + 4 * gq) =
                 make_float4(S[kb][j][0], S[kb][j][1], S[kb][j][2], S[kb][j][3]);
         }
@@ -156,11 +158,17 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][2], 
 // P) and from zero (giving Q), a combine kernel chains S_in through the
 // segments into the tape, and kFwdSegOut reruns every segment from its tape
 // state for o and the final state.
+// kNVB = 1 (training forward only) splits a task's 128 value columns over two
+// workgroups: each wave then owns one 16-column block.  The state path is
+// column-local, so the halves run independently and each repeats the
+// prologue and the 16x16 algebra; for calls with fewer tasks than compute
+// units this halves the state work on each task's critical path.
 constexpr int kFwdTape = 0, kFwdRebuild = 1, kFwdRecords = 2, kFwdInfer = 3, kFwdInferCkpt = 4,
               kFwdSegPQ = 5, kFwdSegOut = 6;
 
-template <int kMode>
+template <int kMode, int kNVB = 2>
 __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
+    static_assert(kNVB == 2 || (kNVB == 1 && kMode == kFwdTape), "column split: training forward only");
     constexpr bool kRebuild = kMode == kFwdRebuild;  // one segment, no output
     constexpr bool kSegPQ = kMode == kFwdSegPQ;
     constexpr bool kSegTask = kRebuild || kSegPQ || kMode == kFwdSegOut;  // one tape segment per task
@@ -173,8 +181,23 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     const int wave = tid >> 6;
 
     int n, h, seg = 0;
+    // (from a scalar copy of the wave index: with the vector one the state
+    // rebuild spills)
+    int vb0 = 2 * __builtin_amdgcn_readfirstlane(wave);  // this wave's first 16-column block
     bool segQ = false;  // kFwdSegPQ: the second half of the grid forms Q, the first P
-    if constexpr (kSegTask) {
+    if constexpr (kNVB == 1) {
+        // the two halves of task i sit 8 blocks apart, so both land on the
+        // same XCD (blocks go round-robin over the eight) and share its L2
+        // for q, k, g and beta; a block past the last task ends here, before
+        // any barrier
+        const int b = blockIdx.x;
+        const int ti = (b >> 4) * 8 + (b & 7);
+        if (ti >= a.num_tasks) return;
+        vb0 = 4 * ((b >> 3) & 1) + __builtin_amdgcn_readfirstlane(wave);
+        const int code = a.plan.task[ti];
+        n = code / a.Hv;
+        h = code - n * a.Hv;
+    } else if constexpr (kSegTask) {
         // item = segment index * Hv + h; the segment list holds (n, j) pairs
         int64_t item = blockIdx.x;
         if constexpr (kSegPQ) {
@@ -223,15 +246,15 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         }
     }
 
-    // state: S^T frags for kb = 0..7 and vb = 2*wave + {0, 1}
-    f32x4 S[8][2];
+    // state: S^T frags for kb = 0..7 and the wave's column blocks vb0 + j
+    f32x4 S[8][kNVB];
     {
         const int lane = tid & 63, gq = lane >> 4, cl = lane & 15;
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int vcol = 16 * (2 * wave + j) + cl;
+            for (int j = 0; j < kNVB; ++j) {
+                const int vcol = 16 * (vb0 + j) + cl;
                 if constexpr (kInfer) {
                     S[kb][j] = from_bf4(*(const bf16x4*)(pinit + vcol * D + 16 * kb + 4 * gq));
                 } else if constexpr (kSegPQ) {
@@ -272,7 +295,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     {
         const int lane = tid & 63;
         load_rows_s(cur, sp, min(cb * CH + (tid >> 4), L - 1), (tid & 15) * 8);
-        load_cols_cf(vcur, sp, cb * CH + 4 * (lane >> 4), L - 1, 32 * wave + (lane & 15));
+        load_cols_cf<kNVB>(vcur, sp, cb * CH + 4 * (lane >> 4), L - 1, 16 * vb0 + (lane & 15));
     }
     __syncthreads();
 
@@ -386,8 +409,8 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
                 for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int vcol = 16 * (2 * wave + j) + cl;
+                    for (int j = 0; j < kNVB; ++j) {
+                        const int vcol = 16 * (vb0 + j) + cl;
                         *(bf16x4*)(dst + vcol * D + 16 * kb + 4 * gq) = to_bf4(S[kb][j]);
                     }
             }
@@ -481,8 +504,9 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         // Y = Kg S0^T and O^T = S0 Qg^T (S0 converted once for both); every
         // wave forms its own, waves 0 and 1 inside their branches so that
         // these MFMAs fill the latency of the substitution
-        f32x4 Y[2] = {zero4(), zero4()};
-        f32x4 OT[2] = {zero4(), zero4()};
+        f32x4 Y[kNVB], OT[kNVB];
+#pragma unroll
+        for (int vb = 0; vb < kNVB; ++vb) Y[vb] = OT[vb] = zero4();
         auto y_ot = [&]() __attribute__((always_inline)) {
             if (precise) {
                 // Y = Kg_hi S0_hi + Kg_hi S0_lo + Kg_lo S0_hi, O^T from S0_hi
@@ -495,10 +519,10 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                     if constexpr (kOut)
                         q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
 #pragma unroll
-                    for (int vb = 0; vb < 2; ++vb) {
+                    for (int vb = 0; vb < kNVB; ++vb) {
                         if constexpr (kRec) {
                             const bf16x4 ident = identity_frag(lane);
-                            const int vbg = 2 * wave + vb;
+                            const int vbg = vb0 + vb;
                             bf16* dst = (bf16*)a.rec_s0 + rec * (D * D) + lane * 4;
                             *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) =
                                 to_bf4(transpose_frag(to_bf4(S[2 * j][vb]), ident));
@@ -517,12 +541,12 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 }
                 return;
             }
-            bf16x8 sb[4][2];
+            bf16x8 sb[4][kNVB];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bf16x8 kg8 = cat8(ld4(&sm.rf_kg[(2 * j) * FS], lane), ld4(&sm.rf_kg[(2 * j + 1) * FS], lane));
 #pragma unroll
-                for (int vb = 0; vb < 2; ++vb) {
+                for (int vb = 0; vb < kNVB; ++vb) {
                     const bf16x4 s0 = to_bf4(S[2 * j][vb]);
                     const bf16x4 s1 = to_bf4(S[2 * j + 1][vb]);
                     sb[j][vb] = cat8(s0, s1);
@@ -531,7 +555,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                         // chunk-start state record: frag (kb, vb) with lane (gq, k)
                         // holding S0[16vb + 4gq + i][16kb + k]
                         const bf16x4 ident = identity_frag(lane);
-                        const int vbg = 2 * wave + vb;
+                        const int vbg = vb0 + vb;
                         bf16* dst = (bf16*)a.rec_s0 + rec * (D * D) + lane * 4;
                         *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) = to_bf4(transpose_frag(s0, ident));
                         *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) = to_bf4(transpose_frag(s1, ident));
@@ -543,7 +567,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 for (int j = 0; j < 4; ++j) {
                     const bf16x8 q8 = cat8(ld4(&sm.rf_qg[(2 * j) * FS], lane), ld4(&sm.rf_qg[(2 * j + 1) * FS], lane));
 #pragma unroll
-                    for (int vb = 0; vb < 2; ++vb) OT[vb] = mma32(sb[j][vb], q8, OT[vb]);   // lane (gq, c): O[c][v=4gq+i]
+                    for (int vb = 0; vb < kNVB; ++vb) OT[vb] = mma32(sb[j][vb], q8, OT[vb]);   // lane (gq, c): O[c][v=4gq+i]
                 }
             }
         };
@@ -656,55 +680,54 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         bf16x8 aq2;
         if constexpr (kOut) aq2 = *(const bf16x8*)&sm.sh_aq[lane * 8];
         // U = Tb V - Tb Y (CF(V) loaded directly)
-        f32x4 U[2];
+        f32x4 U[kNVB];
         {
             if constexpr (kSegPQ) {
                 if (!segQ) {  // P runs with v = 0
-                    vcur.v0 = to_bf4(zero4());
-                    vcur.v1 = to_bf4(zero4());
+#pragma unroll
+                    for (int vb = 0; vb < kNVB; ++vb) vcur.v[vb] = to_bf4(zero4());
                 }
             }
-            const bf16x4 cfv0 = vcur.v0;
-            const bf16x4 cfv1 = vcur.v1;
             // a 16x16x32 costs about what a 16x16x16 does, so the hi/lo
             // products take two: [Tb_hi|Tb_lo] [V;V] and [Tb_hi|Tb_lo] [-Y;-Y]
             // (every operand tuple is formed where it is produced, no copies)
             const bf16x8 tb2 = cat8(tbh, tbl);
-            U[0] = mma32(tb2, cat8(cfv0, cfv0), zero4());
-            U[1] = mma32(tb2, cat8(cfv1, cfv1), zero4());
+#pragma unroll
+            for (int vb = 0; vb < kNVB; ++vb) U[vb] = mma32(tb2, cat8(vcur.v[vb], vcur.v[vb]), zero4());
             if (precise) {   // Y as a hi/lo pair as well: [Tb_hi|Tb_lo] [-Y_hi;-Y_hi] + [-Y_lo;-Y_lo]
 #pragma unroll
-                for (int vb = 0; vb < 2; ++vb) {
+                for (int vb = 0; vb < kNVB; ++vb) {
                     bf16x4 yh, yl;
                     split4(-Y[vb], yh, yl);
                     U[vb] = mma32(tb2, cat8(yh, yh), U[vb]);
                     U[vb] = mma32(tb2, cat8(yl, yl), U[vb]);
                 }
             } else {
-                U[0] = mma32(tb2, cat8(to_bf4_neg(Y[0]), to_bf4_neg(Y[0])), U[0]);
-                U[1] = mma32(tb2, cat8(to_bf4_neg(Y[1]), to_bf4_neg(Y[1])), U[1]);
+#pragma unroll
+                for (int vb = 0; vb < kNVB; ++vb)
+                    U[vb] = mma32(tb2, cat8(to_bf4_neg(Y[vb]), to_bf4_neg(Y[vb])), U[vb]);
             }
         }
-        load_cols_cf(vcur, sp, t0 + CH + 4 * gq, L - 1, 32 * wave + cl);
+        load_cols_cf<kNVB>(vcur, sp, t0 + CH + 4 * gq, L - 1, 16 * vb0 + cl);
         // O^T += U^T Aqk^T, store; then the state update S^T += Kt^T U
         auto out_term = [&](int vb, bf16x4 uh) __attribute__((always_inline)) {
             if constexpr (kRec) {
                 // U record, RF layout: lane (gq, c) holds U[c][16vb + 4gq + i]
                 const bf16x4 ut = to_bf4(transpose_frag(to_bf4(U[vb]), identity_frag(lane)));
-                *(bf16x4*)at((bf16*)a.rec_u + rec * (CH * D), ((2 * wave + vb) * 64 + lane) * 4) = ut;
+                *(bf16x4*)at((bf16*)a.rec_u + rec * (CH * D), ((vb0 + vb) * 64 + lane) * 4) = ut;
             }
             if constexpr (kOut) {
                 // [U_hi|U_hi] against [Aqk/2;Aqk/2]: the chain's last step is a
-                // 16x16x32 as well; lane (gq, c) holds O[c][32w + 16vb + 4gq + i]
+                // 16x16x32 as well; lane (gq, c) holds O[c][16(vb0 + vb) + 4gq + i]
                 OT[vb] = mma32(cat8(uh, uh), aq2, OT[vb]);
                 if (cl < nv) {
                     const bf16x4 ob = to_bf4(OT[vb]);
-                    *(bf16x4*)at(sp.o, __umul24((unsigned)(t0 + cl), sp.sv) + 32 * wave + 16 * vb + 4 * gq) = ob;
+                    *(bf16x4*)at(sp.o, __umul24((unsigned)(t0 + cl), sp.sv) + 16 * (vb0 + vb) + 4 * gq) = ob;
                 }
             }
         };
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb) out_term(vb, to_bf4(U[vb]));
+        for (int vb = 0; vb < kNVB; ++vb) out_term(vb, to_bf4(U[vb]));
         phase_b(ci + 1);
         // S^T += Kt^T U in FP16, [Kt_hi|Kt_lo] (about 22 bits) against [U;U]
         // (11 bits) in one 16x16x32 per state frag; precise chunks add
@@ -717,7 +740,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         // with it (powers of two: exact), and both are scaled back after.
         float um = 0.f;
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb)
+        for (int vb = 0; vb < kNVB; ++vb)
             um = fmaxf(um, fmaxf(fmaxf(fabsf(U[vb][0]), fabsf(U[vb][1])),
                                  fmaxf(fabsf(U[vb][2]), fabsf(U[vb][3]))));
         const bool big = __builtin_amdgcn_ballot_w64(!(um < 16384.f)) != 0;
@@ -729,17 +752,17 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             const float sc = ldexpf(1.f, -e);
             isc = ldexpf(1.f, e);
 #pragma unroll
-            for (int vb = 0; vb < 2; ++vb) U[vb] *= sc;
+            for (int vb = 0; vb < kNVB; ++vb) U[vb] *= sc;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-                for (int vb = 0; vb < 2; ++vb) S[kb][vb] *= sc;
+                for (int vb = 0; vb < kNVB; ++vb) S[kb][vb] *= sc;
         }
         // (a precise chunk parks U's lo part in LDS over the main loop, which
         // then holds no value that only precise chunks need)
-        f16x8 uh8[2];
+        f16x8 uh8[kNVB];
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb) {
+        for (int vb = 0; vb < kNVB; ++vb) {
             f16x4 h, l;
             if (precise) {
                 split4_f16(U[vb], h, l);
@@ -754,16 +777,16 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             const f16x8 t2 = *(const f16x8*)&sm.cf_kt[kb * FS2 + lane * 8];
             const float4 gd = *(const float4*)&sm.gamc[ci & 1][16 * kb + 4 * gq];
 #pragma unroll
-            for (int vb = 0; vb < 2; ++vb) {
+            for (int vb = 0; vb < kNVB; ++vb) {
                 f32x4 s = S[kb][vb];
                 s[0] *= gd.x; s[1] *= gd.y; s[2] *= gd.z; s[3] *= gd.w;
                 S[kb][vb] = mma32h(t2, uh8[vb], s);
             }
         }
         if (precise) {   // + [Kt_hi|Kt_lo] [U_lo;U_lo]
-            f16x8 ul8[2];
+            f16x8 ul8[kNVB];
 #pragma unroll
-            for (int vb = 0; vb < 2; ++vb) {
+            for (int vb = 0; vb < kNVB; ++vb) {
                 const f16x4 l = sm.ulo[wave][vb][lane];
                 ul8[vb] = cat8h(l, l);
             }
@@ -771,19 +794,19 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
             for (int kb = 0; kb < 8; ++kb) {
                 const f16x8 t2 = *(const f16x8*)&sm.cf_kt[kb * FS2 + lane * 8];
 #pragma unroll
-                for (int vb = 0; vb < 2; ++vb) S[kb][vb] = mma32h(t2, ul8[vb], S[kb][vb]);
+                for (int vb = 0; vb < kNVB; ++vb) S[kb][vb] = mma32h(t2, ul8[vb], S[kb][vb]);
             }
         }
         if (big) {
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-                for (int vb = 0; vb < 2; ++vb) S[kb][vb] *= isc;
+                for (int vb = 0; vb < kNVB; ++vb) S[kb][vb] *= isc;
         }
         const int tend = t0 + nv;
         if (kMode == kFwdTape && a.tape != nullptr && tend < L && (tend % a.ck_every) == 0) {
             const int64_t jck = tend / a.ck_every;
-            store_state(a.tape + ((tape_base + jck - 1) * a.Hv + h) * (int64_t)D * D, S, wave, gq, cl);
+            store_state<kNVB>(a.tape + ((tape_base + jck - 1) * a.Hv + h) * (int64_t)D * D, S, vb0, gq, cl);
         }
         rq = rq_next;
         rk = rk_next;
@@ -796,15 +819,15 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int vcol = 16 * (2 * wave + j) + cl;
+            for (int j = 0; j < kNVB; ++j) {
+                const int vcol = 16 * (vb0 + j) + cl;
                 *(bf16x4*)(pslab + vcol * D + 16 * kb + 4 * gq) = to_bf4(S[kb][j]);
             }
     } else if constexpr (kSegPQ) {
         const int64_t segs = a.seg_items / a.Hv;
         const int64_t sj = a.plan.tape_off[n] + n + seg;
         const int64_t si = (segQ ? segs : 0) + sj;
-        store_state(a.seg_out + (si * a.Hv + h) * (int64_t)D * D, S, wave, (tid & 63) >> 4, tid & 15);
+        store_state<kNVB>(a.seg_out + (si * a.Hv + h) * (int64_t)D * D, S, vb0, (tid & 63) >> 4, tid & 15);
         if (!segQ) {
             // P transposed as well (third slab), for the adjoint's chain:
             // lane (gq, cl) holds P[vcol][16kb + 4gq + i]; adjacent lanes
@@ -814,13 +837,13 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < kNVB; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        pt[(16 * kb + 4 * gq + i) * D + 16 * (2 * wave + j) + cl] = S[kb][j][i];
+                        pt[(16 * kb + 4 * gq + i) * D + 16 * (vb0 + j) + cl] = S[kb][j][i];
         }
     } else if (kOut && a.s_final != nullptr && ce == nchunks) {
-        store_state(a.s_final + slab, S, wave, (tid & 63) >> 4, tid & 15);
+        store_state<kNVB>(a.s_final + slab, S, vb0, (tid & 63) >> 4, tid & 15);
     }
 }
 
@@ -835,6 +858,9 @@ hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s) {
     else if (a.rec_s0 != nullptr)
         hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRecords>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0,
                            s, a);
+    else if (a.vsplit)  // two workgroups per task, in groups of 8 tasks (16 blocks)
+        hipLaunchKernelGGL((fwd_chunk_kernel<kFwdTape, 1>), dim3((unsigned)(16 * ((a.num_tasks + 7) / 8))),
+                           dim3(FC_THREADS), 0, s, a);
     else
         hipLaunchKernelGGL(fwd_chunk_kernel<kFwdTape>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0, s,
                            a);

@@ -48,6 +48,9 @@ struct FwdArgs {
     // exceeds precise_log2 runs with hi/lo operands on its whole state path
     // (-inf: every chunk; above 0: none).
     float precise_log2;
+    // Training forward (tape or none): split each task's value columns over
+    // two workgroups (for calls with few tasks)
+    int vsplit;
     // Inference (infer_token_kernel): prologue options and the BF16 state
     // pool [pool_slots][Hv][128][128] read and written in place at slot
     // pool_index[n] (slot n when pool_index is null); s0, s_final and tape

@@ -101,7 +101,7 @@ typedef enum {
     KDA_ROUTE_AUTO = 0,      /* library chooses (see kda_plan_query) */
     KDA_ROUTE_CHUNK = 1,     /* chunked MFMA kernel */
     KDA_ROUTE_ROWSPLIT = 2,  /* per-token FP32 kernel, state rows split across workgroups */
-    KDA_ROUTE_SEGMENTS = 3   /* training forward with the tape context only: the chunked
+    KDA_ROUTE_SEGMENTS = 3,  /* training forward with the tape context only: the chunked
                                 kernel over all tape segments at once.  Each segment's
                                 end state is affine in its start state (S_in P + Q); P
                                 and Q of every segment are formed in parallel, chained
@@ -112,6 +112,14 @@ typedef enum {
                                 AUTO takes it when 2 x segments x Hv <= 768 and the
                                 longest sequence spans 4 or more tape segments.  Without
                                 a context the plain chunked kernel runs. */
+    KDA_ROUTE_CHUNK_SPLIT = 4 /* training forward (tape context or none): the chunked kernel
+                                with each task's 128 value columns split over two
+                                workgroups.  The state path is column-local, so each half
+                                runs on its own and repeats the state-independent work
+                                (prologue, 16x16 algebra); with fewer tasks than compute
+                                units this shortens each task's chain.  Same tape and
+                                backward as KDA_ROUTE_CHUNK.  AUTO takes it when
+                                2 x tasks <= 256 and route 3 is not taken. */
 } kda_route;
 
 /* What the training forward saves for the backward.  TAPE: the FP32 state

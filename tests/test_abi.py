@@ -125,11 +125,19 @@ def test_longest_first_order():
 
 
 def test_route_choice():
-    # the chunked kernel is chosen at every task count; the row-split one on request
-    assert kda.kda_plan_query(_fixed())[0] == kda.ROUTE_CHUNK
-    assert kda.kda_plan_query(kda.make_problem(8, 64, 16, 16, 8))[0] == kda.ROUTE_CHUNK
+    # the chunked kernel at every task count, its column split for 128 tasks
+    # or fewer (two workgroups each); the row-split one on request
+    assert kda.kda_plan_query(_fixed())[0] == kda.ROUTE_CHUNK_SPLIT
+    assert kda.kda_plan_query(kda.make_problem(8, 64, 16, 16, 8))[0] == kda.ROUTE_CHUNK_SPLIT
+    assert kda.kda_plan_query(kda.make_problem(8, 64, 16, 32, 8))[0] == kda.ROUTE_CHUNK
     assert kda.kda_plan_query(_fixed(route=2))[0] == kda.ROUTE_ROWSPLIT
     assert kda.kda_plan_query(_fixed(route=1))[0] == kda.ROUTE_CHUNK
+    assert kda.kda_plan_query(_fixed(route=4))[0] == kda.ROUTE_CHUNK_SPLIT
+    # the per-chunk records need the unsplit kernel
+    p = _fixed(context=kda.CONTEXT_RECORDS)
+    assert kda.kda_plan_query(p)[0] == kda.ROUTE_CHUNK
+    assert _status(kda.kda_plan_query, _fixed(context=kda.CONTEXT_RECORDS, route=4)) == 11
+    assert _status(kda.kda_plan_query, _fixed(route=5)) == 11
 
 
 def test_forward_rejects_overlap_and_null_before_device_work():

@@ -38,7 +38,7 @@ def _small_cases():
     }
 
 
-@pytest.mark.parametrize("route", [1, 2, 3], ids=["fwd-chunk", "fwd-rowsplit", "fwd-segments"])
+@pytest.mark.parametrize("route", [1, 2, 3, 4], ids=["fwd-chunk", "fwd-rowsplit", "fwd-segments", "fwd-split"])
 @pytest.mark.parametrize("case", list(_small_cases().keys()))
 def test_backward_small(case, route):
     (problem, seed), ckpt = _small_cases()[case]

@@ -56,7 +56,7 @@ CASES = {
 
 # route 3: the segment-parallel chunked route through a 64-token tape (it needs
 # the context), whose P and Q runs take the same precise chunks
-@pytest.mark.parametrize("route", [1, 2, 3], ids=["chunk", "rowsplit", "segments"])
+@pytest.mark.parametrize("route", [1, 2, 3, 4], ids=["chunk", "rowsplit", "segments", "split"])
 @pytest.mark.parametrize("case", list(CASES.keys()))
 def test_forward_edge(case, route):
     problem, seed, set_to = CASES[case]
@@ -135,7 +135,7 @@ def test_backward_edge(case, route):
     pu.report_and_check(list(zip(pu.GRAD_NAMES, got, ref)))
 
 
-@pytest.mark.parametrize("route", [1, 2], ids=["chunk", "rowsplit"])
+@pytest.mark.parametrize("route", [1, 2, 4], ids=["chunk", "rowsplit", "split"])
 def test_long_single_sequence(route):
     """One 4096-token sequence and one head: a single task, 256 chunks in
     sequence on the chunked route, 4096 steps on the row-split route."""
@@ -151,7 +151,7 @@ def test_long_single_sequence(route):
     pu.report_and_check(list(zip(pu.GRAD_NAMES, got, ref)))
 
 
-@pytest.mark.parametrize("route", [1, 3], ids=["chunk", "segments"])
+@pytest.mark.parametrize("route", [1, 3, 4], ids=["chunk", "segments", "split"])
 def test_forward_huge_values(route):
     """Values of order 1e5: U leaves FP16's range, so the plain chunks' FP16
     state update scales U (and the state with it) by a power of two for the

@@ -15,8 +15,8 @@ from tests import parity_util as pu
 
 pytestmark = pytest.mark.gpu
 
-ROUTES = [1, 2]  # chunked MFMA, row-split
-ROUTE_NAMES = {1: "chunk", 2: "rowsplit"}
+ROUTES = [1, 2, 4]  # chunked MFMA, row-split, chunked with the value columns split
+ROUTE_NAMES = {1: "chunk", 2: "rowsplit", 4: "split"}
 
 
 def _small_cases():
