@@ -423,7 +423,7 @@ def recurrent_kda_training_backward(context: RecurrentKDATrainingContext, do, df
 # inference API (decode and prefill on a state pool)
 # ---------------------------------------------------------------------------
 def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initial_state=None,
-                  use_qk_l2norm_in_kernel: bool = True, use_gate_in_kernel: bool = False,
+                  output_final_state: bool = False, use_qk_l2norm_in_kernel: bool = True, use_gate_in_kernel: bool = False,
                   lower_bound=None, cu_seqlens=None, ssm_state_indices=None,
                   num_spec_tokens: Optional[int] = None, num_accepted_tokens=None,
                   output=None, initial_state_source=None, initial_state_indices=None,
@@ -432,15 +432,17 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
                   cu_seqlens_cpu=None, ssm_state_indices_cpu=None, checkpoint_cu_starts_cpu=None,
                   initial_state_indices_cpu=None, route: int = ROUTE_AUTO):
     """Decode / prefill subset of page "flashinfer.kda.recurrent_kda": returns
-    (output, initial_state) with initial_state, a BF16 state pool
+    (output, final_state).  initial_state is a BF16 state pool
     [P, Hv, 128, 128], updated in place (slot ssm_state_indices[n] for sequence
-    n, or slot n).  Packed calls pass cu_seqlens (int64) with its CPU mirror,
+    n, or slot n); None starts every sequence from zero in a new pool of N
+    slots (not with ssm_state_indices or speculative decode).  final_state is
+    that pool when output_final_state is set, else None.  Packed calls pass cu_seqlens (int64) with its CPU mirror,
     and indices with theirs.  route: ROUTE_AUTO, ROUTE_CHUNK (needs every
     per-token log-decay >= -5) or ROUTE_ROWSPLIT (token-serial, any gate).
     With checkpoint_every_n_tokens = E > 0, state_checkpoints (BF16
     [C, Hv, 128, 128]) receives, from row checkpoint_cu_starts[n] on, the
     states of sequence n before tokens 0, E, 2E, ... and the call returns
-    (output, initial_state, state_checkpoints).  Speculative decode
+    (output, final_state, state_checkpoints).  Speculative decode
     (num_spec_tokens = S): every sequence has 1+S tokens, ssm_state_indices is
     [N, 1+S]; the state starts from slot [n, a-1] with a =
     num_accepted_tokens[n] clamped to [1, 1+S] (1 when omitted) and the state
@@ -463,7 +465,11 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
         N = cu_seqlens.numel() - 1
     else:
         N = B
-    _require(initial_state is not None, "initial_state (the BF16 state pool) is required")
+    S = int(num_spec_tokens or 0)
+    if initial_state is None:
+        _require(ssm_state_indices is None and S == 0,
+                 "ssm_state_indices and speculative decode need an initial_state pool")
+        initial_state = torch.zeros((N, Hv, 128, 128), dtype=torch.bfloat16, device=dev)
     _require(initial_state.dim() == 4 and tuple(initial_state.shape[1:]) == (Hv, 128, 128),
              "initial_state must be [P, Hv, 128, 128]")
     P = initial_state.shape[0]
@@ -479,7 +485,6 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
     if dt_bias is not None:
         dt_bias = dt_bias.reshape(Hv, 128) if dt_bias.dim() == 1 else dt_bias
         _check_tensor("dt_bias", dt_bias, torch.float32, (Hv, 128), dev)
-    S = int(num_spec_tokens or 0)
     if ssm_state_indices is not None:
         _require(ssm_state_indices_cpu is not None, "ssm_state_indices needs its CPU mirror")
         _check_tensor("ssm_state_indices", ssm_state_indices, torch.int32,
@@ -519,6 +524,7 @@ def recurrent_kda(q, k, v, g, beta, A_log=None, dt_bias=None, scale=None, initia
         p.source_indices = _ptr(initial_state_indices)
         p.source_indices_host = _ptr(initial_state_indices_cpu)
     kda_infer(p, q, k, v, g, beta, A_log, dt_bias, initial_state, o)
+    final = initial_state if output_final_state else None
     if checkpoint_every_n_tokens:
-        return o, initial_state, state_checkpoints
-    return o, initial_state
+        return o, final, state_checkpoints
+    return o, final

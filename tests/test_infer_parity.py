@@ -98,7 +98,8 @@ def _run_case(name, route):
         cu_seqlens=None if inp.cu_seqlens is None else inp.cu_seqlens.to(dev),
         cu_seqlens_cpu=inp.cu_seqlens,
         ssm_state_indices=None if idx_cpu is None else idx_cpu.to(dev),
-        ssm_state_indices_cpu=idx_cpu, route=ROUTES[route], **_binding_opts(opts))
+        ssm_state_indices_cpu=idx_cpu, route=ROUTES[route], output_final_state=True,
+        **_binding_opts(opts))
     torch.cuda.synchronize()
     assert pool_out.data_ptr() == pool_dev.data_ptr()
     o_ref, pool_ref = kio.infer_forward(
@@ -374,3 +375,31 @@ def test_infer_long_single_sequence(route):
                                         lengths=problem.lengths, packed=True, **gref)
     pu.report_and_check([("o", o.float().cpu().numpy(), o_ref),
                          ("state_pool", pool.float().cpu().numpy(), pool_ref)])
+
+
+@pytest.mark.parametrize("route", list(ROUTES.keys()))
+def test_infer_without_initial_state(route):
+    """Page "flashinfer.kda.recurrent_kda", parameters initial_state (None:
+    zero-initialised) and output_final_state (the final state is returned only
+    when asked for): a call without a pool equals one on an explicit zero pool
+    of N slots."""
+    import gated_delta_rule_32_amd as kda
+    problem = workloads.Problem([5, 40, 17], 2, 4, packed=True)
+    inp = workloads.make_infer_inputs(problem, 77, problem.N, **_gate_gen(route))
+    dev = torch.device("cuda")
+    print(f"[infer] no initial state route={route}", flush=True)
+    gcall, _ = _gate_kw(route, inp, dev)
+    args = (inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.g.to(dev), inp.beta.to(dev))
+    kw = dict(cu_seqlens=inp.cu_seqlens.to(dev), cu_seqlens_cpu=inp.cu_seqlens, route=ROUTES[route],
+              **gcall)
+    o_a, s_a = kda.recurrent_kda(*args, **kw)
+    assert s_a is None
+    o_b, s_b = kda.recurrent_kda(*args, output_final_state=True, **kw)
+    zero = torch.zeros((problem.N, problem.Hv, 128, 128), dtype=torch.bfloat16, device=dev)
+    o_c, s_c = kda.recurrent_kda(*args, initial_state=zero, output_final_state=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_c) and torch.equal(o_b, o_c) and torch.equal(s_b, s_c)
+    assert s_c.data_ptr() == zero.data_ptr()
+    with pytest.raises(ValueError):
+        kda.recurrent_kda(*args, ssm_state_indices=torch.arange(problem.N, dtype=torch.int32, device=dev),
+                          ssm_state_indices_cpu=torch.arange(problem.N, dtype=torch.int32), **kw)
