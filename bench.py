@@ -35,10 +35,11 @@ FWD_SOURCES = ["gated_delta_rule_32_amd/csrc/kda_fwd_chunk.hip",
                "gated_delta_rule_32_amd/csrc/kda_kernels.h"]
 
 
-ROUTE_NAMES = {1: "chunk", 2: "rowsplit", 3: "segments"}
+ROUTE_NAMES = {1: "chunk", 2: "rowsplit", 3: "segments", 4: "chunk-split"}
 ROUTE_KERNELS = {1: "fwd_chunk_kernel", 2: "fwd_rowsplit_kernel",
                  3: "fwd_chunk_kernel over all tape segments (P and Q, seg_combine_kernel, rerun): "
-                    "the whole forward's time"}
+                    "the whole forward's time",
+                 4: "fwd_chunk_kernel with the value columns split over two workgroups per task"}
 
 
 def fwd_source_sha() -> str:
