@@ -165,8 +165,9 @@ def _make_from_gen(problem: Problem, gen, with_adjoints: bool) -> Inputs:
 
 def make_inputs_on_device(problem: Problem, seed: int, device, with_adjoints: bool = True) -> Inputs:
     """The same recipe drawn by a generator on `device` (fast for large
-    benchmark shapes; the values differ from the CPU draws of the same seed,
-    the distributions do not).  Used for timing only, never for parity."""
+    shapes; the values differ from the CPU draws of the same seed, the
+    distributions do not).  Used for timing, and by the maximum-size parity
+    test, which copies the sampled tasks' values back for the oracle."""
     gen = torch.Generator(device=device).manual_seed(seed)
     B, T, Hqk, Hv, N = problem.B, problem.T, problem.Hqk, problem.Hv, problem.N
 
