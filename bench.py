@@ -161,8 +161,8 @@ def cpu_baseline(inp, max_seconds: float = 30.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="packed")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
