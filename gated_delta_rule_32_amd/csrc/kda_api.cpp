@@ -749,9 +749,15 @@ kda_status kda_fwd_noalloc(const kda_problem* pp, const void* q, const void* k, 
     void* scratch = nullptr;
     e = kda::noalloc_scratch(dev, &scratch);
     if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
-    std::vector<char> host(lay.bytes);
-    fill_plan(p, lay, host.data());
-    e = kda::upload_to_scratch(scratch, host.data(), lay.bytes, stream);
+    {
+        // the schedule is built in a static host buffer (no heap allocation)
+        // and handed over as kernel arguments, which the launch copies
+        static unsigned char host[KDA_NOALLOC_SCRATCH_BYTES];
+        static std::mutex host_mu;
+        std::lock_guard<std::mutex> lock(host_mu);
+        fill_plan(p, lay, (char*)host);
+        e = kda::upload_to_scratch(scratch, host, lay.bytes, stream);
+    }
     if (e != hipSuccess) return hip_fail(e, "schedule upload launch");
     return fwd_launch(p, dev, scratch, lay, q, k, v, g, beta, A_log, dt_bias, initial_state, o,
                       final_state, ctx, ctx_bytes, stream);

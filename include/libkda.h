@@ -225,8 +225,11 @@ kda_status kda_fwd(const kda_problem* p,
  * arguments, checks, kernels and results as kda_fwd, but the schedule (task
  * order, sequence and tape offsets, segment list) goes into a static device
  * array of KDA_NOALLOC_SCRATCH_BYTES per device instead of library-allocated
- * memory, written by small kernel launches on `stream` (no hipMalloc, no
- * pinned host memory, no memset).  A problem whose schedule needs more than
+ * memory, written by small kernel launches on `stream` that carry it as
+ * arguments (no hipMalloc or hipFree, no pinned host memory, no memset or
+ * copy; the schedule is assembled in a static host buffer, and only the
+ * argument checks and the ordering use small C++ heap allocations, as in
+ * kda_fwd).  A problem whose schedule needs more than
  * that (about 900k (sequence, value head) tasks) is refused with
  * KDA_ERR_WORKSPACE_SIZE before any device work.  Every call on a device
  * shares that device's array and overwrites it: calls that overlap on one
