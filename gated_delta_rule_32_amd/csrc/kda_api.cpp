@@ -796,11 +796,12 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
         if (r.key != plan_key(p, dev) || r.B != p.B || r.T != p.T || r.Hqk != p.Hqk ||
             r.Hv != p.Hv || r.N != p.N || r.ctxmode != p.ctxmode)
             return fail(KDA_ERR_CTX_MISMATCH, "context was made for another shape or device");
-        // the backward reads what its route's forward stored (the
-        // segment-parallel one also reads P^T after the tape)
-        if (r.route != p.route)
-            return fail(KDA_ERR_CTX_MISMATCH, "context was filled on route %d, the backward resolves to %d",
-                        r.route, p.route);
+        // every forward route leaves the same tape; the segment-parallel
+        // backward also reads the transfer matrices P^T that only the
+        // segment-parallel forward stores after it
+        if (p.route == 3 && r.route != 3)
+            return fail(KDA_ERR_CTX_MISMATCH, "context was filled on route %d, the backward resolves to %d "
+                        "(segment-parallel), which needs that route's forward", r.route, p.route);
         if (std::memcmp(r.ptrs, ptrs, sizeof(ptrs)) != 0)
             return fail(KDA_ERR_CTX_MISMATCH, "inputs differ from the forward that made the context");
         if (r.stream != stream)

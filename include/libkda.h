@@ -246,7 +246,9 @@ kda_status kda_fwd_noalloc(const kda_problem* p,
  * and "flashinfer.kda_training", paragraph 5).  Takes the same problem and
  * input pointers as the kda_fwd that filled ctx (checked against the host
  * record of that call, together with the device and the stream: a context is
- * used on the stream that created it), the adjoints d_o and dfinal_state, and
+ * used on the stream that created it; any route may consume the tape, except
+ * that the segment-parallel backward needs a segment-parallel forward), the
+ * adjoints d_o and dfinal_state, and
  * writes the eight gradients.  dq/dk sum over the value heads that share a
  * q/k head; dA_log/ddt_bias sum over all sequences and tokens.  The
  * workspace is caller-owned scratch of kda_bwd_workspace_bytes() bytes.

@@ -72,7 +72,8 @@ def _bwd(kda, p, d, ctx, grads, ws, **over):
 def test_route_mismatch_is_refused():
     """A forward forced onto the plain chunked route fills a context sized for
     the automatic (segment-parallel) route; the automatic backward must refuse
-    it, and a backward on the forward's own route accepts it."""
+    it (it would read transfer matrices that forward never stored), and a
+    backward on any route that reads only the tape accepts it."""
     import gated_delta_rule_32_amd as kda
     problem = P([1024], 1, 1, packed=False)
     p_auto = kda.make_problem(1, 1024, 1, 1, 1)
@@ -86,6 +87,11 @@ def test_route_mismatch_is_refused():
     p1 = kda.make_problem(1, 1024, 1, 1, 1, route=kda.ROUTE_CHUNK)
     assert _bwd(kda, p1, d, ctx, grads, ws) == 0
     torch.cuda.synchronize()
+    ref = [g.clone() for g in grads]
+    p4 = kda.make_problem(1, 1024, 1, 1, 1, route=kda.ROUTE_CHUNK_SPLIT)
+    assert _bwd(kda, p4, d, ctx, grads, ws) == 0
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(grads, ref))
 
 
 def test_stream_and_pointer_mismatch_are_refused():
