@@ -586,7 +586,7 @@ static WsLayout ws_layout(const Prob& p) {
     w.ta = r.ta;
     size_t off = r.end;
     w.dqk = off;
-    if (p.G > 1) off = align256(off + (size_t)p.tokens * p.Hv * 2 * D * sizeof(float));
+    if (p.G > 1) off = align256(off + (size_t)p.tokens * p.Hv * 2 * D * sizeof(uint16_t));
     w.par = off;
     // parameter partials per task, or per (segment, head) on the segment-parallel route
     const bool segs = p.route == 3 && p.ctxmode == KDA_CONTEXT_TAPE;
@@ -847,7 +847,7 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
     b.d_o = d_o; b.dfinal = dfinal_state;
     b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg; b.dbeta = dbeta;
     b.dA_log = dA_log; b.ddt_bias = ddt_bias; b.dinit = dinitial_state;
-    b.dqk_part = p.G > 1 ? (float*)(ws + wl.dqk) : nullptr;
+    b.dqk_part = p.G > 1 ? (kda::bf16_t*)(ws + wl.dqk) : nullptr;
     b.dparam_part = (float*)(ws + wl.par);
     b.total_tokens = p.tokens;
 

@@ -176,7 +176,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     bf16* const dqp = (bf16*)b.dq + qk0;
     bf16* const dkp = (bf16*)b.dk + qk0;
     bf16* const dbetap = (bf16*)b.dbeta + bh0;
-    float* const dqkp = b.dqk_part != nullptr ? b.dqk_part + vh0 * 2 : nullptr;
+    bf16* const dqkp = b.dqk_part != nullptr ? (bf16*)b.dqk_part + vh0 * 2 : nullptr;
     // one token row (8 channels at c8) of q, k, g and its beta logit
     auto load_row = [&](RowIn& x, int t, int c8) __attribute__((always_inline)) {
         const unsigned oq = __umul24((unsigned)t, sq) + c8;
@@ -698,9 +698,9 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
                         *(bf16x4*)at(dqp, oq + koff) = to_bf4(dq);
                         *(bf16x4*)at(dkp, oq + koff) = to_bf4(dk);
                     } else {
-                        float* pp = dqkp + 2 * ov + koff;
-                        *(float4*)pp = make_float4(dq[0], dq[1], dq[2], dq[3]);
-                        *(float4*)(pp + D) = make_float4(dk[0], dk[1], dk[2], dk[3]);
+                        bf16* pp = dqkp + 2 * ov + koff;
+                        *(bf16x4*)pp = to_bf4(dq);
+                        *(bf16x4*)(pp + D) = to_bf4(dk);
                     }
                 }
             }
@@ -778,8 +778,8 @@ __global__ void bwd_dqk_reduce_kernel(BwdArgs b, int64_t items) {
     const int64_t tok = rest / a.Hqk;
     f32x4 s = zero4();
     for (int g = 0; g < a.G; ++g) {
-        const float* pp = b.dqk_part + (tok * a.Hv + hq * a.G + g) * (2 * D) + which * D + 4 * grp;
-        s += ld4f(pp);
+        const bf16* pp = (const bf16*)b.dqk_part + (tok * a.Hv + hq * a.G + g) * (2 * D) + which * D + 4 * grp;
+        s += from_bf4(*(const bf16x4*)pp);
     }
     bf16* out = (bf16*)(which == 0 ? b.dq : b.dk);
     *(bf16x4*)(out + (tok * a.Hqk + hq) * D + 4 * grp) = to_bf4(s);

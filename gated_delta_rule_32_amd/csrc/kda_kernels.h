@@ -90,7 +90,7 @@ struct BwdArgs {
     const float* dfinal;
     void* dq; void* dk; void* dv; void* dg; void* dbeta;
     float* dA_log; float* ddt_bias; float* dinit;
-    float* dqk_part;        // [tokens][Hv][2][128] FP32 partial dq,dk when G > 1; else null
+    bf16_t* dqk_part;       // [tokens][Hv][2][128] BF16 partial dq,dk when G > 1; else null
     float* dparam_part;     // [tasks][2][128]: per-task ddt_bias and dA_log partial sums
     int64_t total_tokens;
     // Segment-parallel adjoint (seg_pass 1 or 2; 0: whole tasks).  Tasks are

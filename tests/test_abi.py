@@ -99,10 +99,10 @@ def test_context_and_workspace_sizes():
     chunks = sum((L + 15) // 16 for L in (300, 1, 511))
     ws = kda.kda_bwd_workspace_bytes(p)
     # per (chunk, value head): BF16 chunk-start state, BF16 U, FP32 T/Akk/Aqk;
-    # FP32 dq/dk partials per token and value head (G = 2); per-task partials
+    # BF16 dq/dk partials per token and value head (G = 2); per-task partials
     rec = 128 * 128 * 2 + 16 * 128 * 2 + 3 * 16 * 16 * 4
     tasks = 3 * 2
-    need = chunks * 2 * rec + 812 * 2 * 2 * 128 * 4 + tasks * 2 * 128 * 4
+    need = chunks * 2 * rec + 812 * 2 * 2 * 128 * 2 + tasks * 2 * 128 * 4
     assert need <= ws <= need + 16 * 256
 
 
