@@ -32,6 +32,7 @@ SOURCES = [
     "kda_api.cpp",
     "kda_fwd_rowsplit.hip",
     "kda_fwd_chunk.hip",
+    "kda_fwd_pipe.hip",
     "kda_bwd.hip",
     "kda_infer.hip",
     "kda_noalloc.hip",

@@ -76,20 +76,25 @@ constexpr int64_t kSplitMax = 256;
 
 int auto_route(const Prob& p) {
     // The chunked MFMA kernel.  With few tasks its one workgroup per task
-    // leaves most compute units idle.  When every tape segment's P and Q run
-    // fit in one round (2 x segments x Hv <= 768) and the longest sequence
-    // has at least 4 segments, the segment-parallel form (about 2.5x the
-    // work, spread over the segments) finishes first.  The row-split kernel
-    // is slower per token than one chunked workgroup (2 x 2048 tokens x 16
-    // heads: 1.05 ms against 0.35 ms) and stays selectable as an FP32
-    // reference route.
+    // leaves most compute units idle, and two other forms use them:
+    //   - at most half as many tasks as compute units: two workgroups per
+    //     task over half the value columns each, with producer waves that
+    //     prepare four chunks ahead of the state path (about 1.6 us per
+    //     chunk of the longest sequence);
+    //   - when every tape segment's P and Q runs fit in one round (2 x
+    //     segments x Hv <= 768): the segment-parallel form, about 2.5x the
+    //     work spread over the segments, whose time grows with the segment
+    //     length rather than the sequence length.  It finishes first once
+    //     the longest sequence spans more than 4 segments (3 when the column
+    //     split does not apply); its backward is segment-parallel as well.
+    // The row-split kernel is slower per token than one chunked workgroup
+    // (2 x 2048 tokens x 16 heads: 1.05 ms against 0.35 ms) and stays
+    // selectable as an FP32 reference route.
+    const bool split = p.ctxmode == KDA_CONTEXT_TAPE && 2 * p.num_tasks <= kSplitMax;
     if (p.ctxmode == KDA_CONTEXT_TAPE && 2 * p.total_segs * p.Hv <= kChunkSlots &&
-        p.max_len > 3 * (int64_t)p.ck)
+        p.max_len > (split ? 4 : 3) * (int64_t)p.ck)
         return 3;
-    // At most half as many tasks as compute units: two workgroups per task,
-    // each over half the value columns, so that the state work on each
-    // task's chain halves.
-    if (p.ctxmode == KDA_CONTEXT_TAPE && 2 * p.num_tasks <= kSplitMax) return 4;
+    if (split) return 4;
     return 1;
 }
 

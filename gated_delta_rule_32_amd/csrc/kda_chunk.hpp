@@ -48,6 +48,57 @@ __device__ __forceinline__ void store_cf16(bf16* slots, int r, int c8, bf16x4 lo
     }
 }
 
+struct ColIn {   // V for the wave's 16-column blocks: CF(V)[vb0], CF(V)[vb0+1]
+    bf16x4 v[2];
+};
+
+// Per-task base pointers (uniform, so they live in scalar registers) and
+// element strides; a token row inside the sequence is then a 32-bit offset
+// (the host rejects sequences whose span exceeds 2^31 elements).
+struct SeqPtrs {
+    const bf16* q;   // q[tok0][hq][0]; k likewise
+    const bf16* k;
+    const bf16* g;   // g[tok0][h][0]; v and o likewise
+    const bf16* v;
+    bf16* o;
+    const bf16* beta;  // beta[tok0][h]
+    unsigned sq, sv, sb;  // per-token strides: Hqk*128, Hv*128, Hv
+};
+
+__device__ __forceinline__ void load_rows_s(RowIn& x, const SeqPtrs& p, unsigned t, unsigned c8) {
+    const unsigned oq = __umul24(t, p.sq) + c8;
+    x.q = *(const bf16x8*)at(p.q, oq);
+    x.k = *(const bf16x8*)at(p.k, oq);
+    x.g = *(const bf16x8*)at(p.g, __umul24(t, p.sv) + c8);
+    x.b = *at(p.beta, __umul24(t, p.sb));
+}
+// CF(V) straight from memory: lane (gq, n) takes tokens t4 .. t4+3 (t4 =
+// t0 + 4gq, each clamped to the sequence's last token, whose rows the
+// chunk's zero beta then masks) of channels ch, ch + 16, ...: 2-byte loads
+// into the halves of four registers per block, no transpose.
+template <int NVB>
+__device__ __forceinline__ void load_cols_cf(ColIn& x, const SeqPtrs& p, int t4, int last, unsigned ch) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned o = __umul24((unsigned)min(t4 + i, last), p.sv) + ch;
+#pragma unroll
+        for (int j = 0; j < NVB; ++j) x.v[j][i] = *at(p.v, o + 16 * j);
+    }
+}
+
+template <int NVB>
+__device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][NVB], int vb0, int gq,
+                                            int cl) {
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+        for (int j = 0; j < NVB; ++j) {
+            const int vcol = 16 * (vb0 + j) + cl;
+            *(float4*)(dst + (int64_t)vcol * D + 16 * kb + 4 * gq) =
+                make_float4(S[kb][j][0], S[kb][j][1], S[kb][j][2], S[kb][j][3]);
+        }
+}
+
 // Broadcast lane q of every quad to the whole quad (DPP quad_perm [q,q,q,q]);
 // q must fold to a constant.
 __device__ __forceinline__ float quad_bcast(float x, int q) {

@@ -83,57 +83,6 @@ struct FwdLds {
     int precise[2];                   // by chunk parity: the chunk runs precise
 };
 
-struct ColIn {   // V for the wave's 16-column blocks: CF(V)[vb0], CF(V)[vb0+1]
-    bf16x4 v[2];
-};
-
-// Per-task base pointers (uniform, so they live in scalar registers) and
-// element strides; a token row inside the sequence is then a 32-bit offset
-// (the host rejects sequences whose span exceeds 2^31 elements).
-struct SeqPtrs {
-    const bf16* q;   // q[tok0][hq][0]; k likewise
-    const bf16* k;
-    const bf16* g;   // g[tok0][h][0]; v and o likewise
-    const bf16* v;
-    bf16* o;
-    const bf16* beta;  // beta[tok0][h]
-    unsigned sq, sv, sb;  // per-token strides: Hqk*128, Hv*128, Hv
-};
-
-__device__ __forceinline__ void load_rows_s(RowIn& x, const SeqPtrs& p, unsigned t, unsigned c8) {
-    const unsigned oq = __umul24(t, p.sq) + c8;
-    x.q = *(const bf16x8*)at(p.q, oq);
-    x.k = *(const bf16x8*)at(p.k, oq);
-    x.g = *(const bf16x8*)at(p.g, __umul24(t, p.sv) + c8);
-    x.b = *at(p.beta, __umul24(t, p.sb));
-}
-// CF(V) straight from memory: lane (gq, n) takes tokens t4 .. t4+3 (t4 =
-// t0 + 4gq, each clamped to the sequence's last token, whose rows the
-// chunk's zero beta then masks) of channels ch, ch + 16, ...: 2-byte loads
-// into the halves of four registers per block, no transpose.
-template <int NVB>
-__device__ __forceinline__ void load_cols_cf(ColIn& x, const SeqPtrs& p, int t4, int last, unsigned ch) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const unsigned o = __umul24((unsigned)min(t4 + i, last), p.sv) + ch;
-#pragma unroll
-        for (int j = 0; j < NVB; ++j) x.v[j][i] = *at(p.v, o + 16 * j);
-    }
-}
-
-template <int NVB>
-__device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][NVB], int vb0, int gq,
-                                            int cl) {
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-        for (int j = 0; j < NVB; ++j) {
-            const int vcol = 16 * (vb0 + j) + cl;
-            *(float4*)(dst + (int64_t)vcol * D + 16 * kb + 4 * gq) =
-                make_float4(S[kb][j][0], S[kb][j][1], S[kb][j][2], S[kb][j][3]);
-        }
-}
-
 }  // namespace
 
 // kMode = kFwdTape: the training forward over whole tasks (o, final state, the
@@ -158,17 +107,12 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[8][NVB]
 // P) and from zero (giving Q), a combine kernel chains S_in through the
 // segments into the tape, and kFwdSegOut reruns every segment from its tape
 // state for o and the final state.
-// kNVB = 1 (training forward only) splits a task's 128 value columns over two
-// workgroups: each wave then owns one 16-column block.  The state path is
-// column-local, so the halves run independently and each repeats the
-// prologue and the 16x16 algebra; for calls with fewer tasks than compute
-// units this halves the state work on each task's critical path.
 constexpr int kFwdTape = 0, kFwdRebuild = 1, kFwdRecords = 2, kFwdInfer = 3, kFwdInferCkpt = 4,
               kFwdSegPQ = 5, kFwdSegOut = 6;
 
-template <int kMode, int kNVB = 2>
+template <int kMode>
 __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
-    static_assert(kNVB == 2 || (kNVB == 1 && kMode == kFwdTape), "column split: training forward only");
+    constexpr int kNVB = 2;  // 16-column blocks per wave
     constexpr bool kRebuild = kMode == kFwdRebuild;  // one segment, no output
     constexpr bool kSegPQ = kMode == kFwdSegPQ;
     constexpr bool kSegTask = kRebuild || kSegPQ || kMode == kFwdSegOut;  // one tape segment per task
@@ -185,19 +129,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     // rebuild spills)
     int vb0 = 2 * __builtin_amdgcn_readfirstlane(wave);  // this wave's first 16-column block
     bool segQ = false;  // kFwdSegPQ: the second half of the grid forms Q, the first P
-    if constexpr (kNVB == 1) {
-        // the two halves of task i sit 8 blocks apart, so both land on the
-        // same XCD (blocks go round-robin over the eight) and share its L2
-        // for q, k, g and beta; a block past the last task ends here, before
-        // any barrier
-        const int b = blockIdx.x;
-        const int ti = (b >> 4) * 8 + (b & 7);
-        if (ti >= a.num_tasks) return;
-        vb0 = 4 * ((b >> 3) & 1) + __builtin_amdgcn_readfirstlane(wave);
-        const int code = a.plan.task[ti];
-        n = code / a.Hv;
-        h = code - n * a.Hv;
-    } else if constexpr (kSegTask) {
+    if constexpr (kSegTask) {
         // item = segment index * Hv + h; the segment list holds (n, j) pairs
         int64_t item = blockIdx.x;
         if constexpr (kSegPQ) {
@@ -858,9 +790,8 @@ hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s) {
     else if (a.rec_s0 != nullptr)
         hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRecords>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0,
                            s, a);
-    else if (a.vsplit)  // two workgroups per task, in groups of 8 tasks (16 blocks)
-        hipLaunchKernelGGL((fwd_chunk_kernel<kFwdTape, 1>), dim3((unsigned)(16 * ((a.num_tasks + 7) / 8))),
-                           dim3(FC_THREADS), 0, s, a);
+    else if (a.vsplit)  // two workgroups per task, producer and consumer waves
+        return launch_fwd_pipe(a, s);
     else
         hipLaunchKernelGGL(fwd_chunk_kernel<kFwdTape>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0, s,
                            a);

@@ -110,6 +110,7 @@ struct BwdArgs {
 hipError_t launch_fwd_rowsplit(const FwdArgs& a, hipStream_t s);
 hipError_t launch_infer_token(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_pipe(const FwdArgs& a, hipStream_t s);
 hipError_t launch_state_rebuild(const FwdArgs& a, int64_t num_items, hipStream_t s);
 hipError_t launch_fwd_segments(const FwdArgs& a, int N, hipStream_t s);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t s);

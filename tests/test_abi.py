@@ -130,6 +130,12 @@ def test_route_choice():
     assert kda.kda_plan_query(_fixed())[0] == kda.ROUTE_CHUNK_SPLIT
     assert kda.kda_plan_query(kda.make_problem(8, 64, 16, 16, 8))[0] == kda.ROUTE_CHUNK_SPLIT
     assert kda.kda_plan_query(kda.make_problem(8, 64, 16, 32, 8))[0] == kda.ROUTE_CHUNK
+    # few tasks with long sequences: the segment-parallel route once the
+    # longest sequence spans more than 4 tape segments, the column split
+    # up to that
+    assert kda.kda_plan_query(kda.make_problem(2, 2048, 16, 16, 2))[0] == kda.ROUTE_SEGMENTS
+    assert kda.kda_plan_query(kda.make_problem(8, 1024, 12, 12, 8))[0] == kda.ROUTE_CHUNK_SPLIT
+    assert kda.kda_plan_query(kda.make_problem(8, 1024, 24, 24, 8))[0] == kda.ROUTE_CHUNK
     assert kda.kda_plan_query(_fixed(route=2))[0] == kda.ROUTE_ROWSPLIT
     assert kda.kda_plan_query(_fixed(route=1))[0] == kda.ROUTE_CHUNK
     assert kda.kda_plan_query(_fixed(route=4))[0] == kda.ROUTE_CHUNK_SPLIT

@@ -75,8 +75,8 @@ def test_route_mismatch_is_refused():
     it (it would read transfer matrices that forward never stored), and a
     backward on any route that reads only the tape accepts it."""
     import gated_delta_rule_32_amd as kda
-    problem = P([1024], 1, 1, packed=False)
-    p_auto = kda.make_problem(1, 1024, 1, 1, 1)
+    problem = P([2048], 1, 1, packed=False)
+    p_auto = kda.make_problem(1, 2048, 1, 1, 1)
     assert kda.kda_plan_query(p_auto)[0] == kda.ROUTE_SEGMENTS
     print("[misuse] route mismatch", flush=True)
     inp, d, ctx = _setup(problem, route=kda.ROUTE_CHUNK, ctx_route=kda.ROUTE_AUTO)
@@ -84,11 +84,11 @@ def test_route_mismatch_is_refused():
     grads = _grads(d)
     assert _bwd(kda, p_auto, d, ctx, grads, ws) == MISMATCH
     assert "route" in kda.kda_last_error()
-    p1 = kda.make_problem(1, 1024, 1, 1, 1, route=kda.ROUTE_CHUNK)
+    p1 = kda.make_problem(1, 2048, 1, 1, 1, route=kda.ROUTE_CHUNK)
     assert _bwd(kda, p1, d, ctx, grads, ws) == 0
     torch.cuda.synchronize()
     ref = [g.clone() for g in grads]
-    p4 = kda.make_problem(1, 1024, 1, 1, 1, route=kda.ROUTE_CHUNK_SPLIT)
+    p4 = kda.make_problem(1, 2048, 1, 1, 1, route=kda.ROUTE_CHUNK_SPLIT)
     assert _bwd(kda, p4, d, ctx, grads, ws) == 0
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(grads, ref))

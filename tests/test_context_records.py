@@ -1,8 +1,9 @@
 """GPU parity of the per-chunk records context (the forward stores every
 chunk's records, the backward reruns no forward recurrence), through the C
-ABI.  The records are the same arithmetic as the tape context's rebuilt ones,
-so o, the final state and all eight gradients must equal the tape context's
-bit for bit; they are also checked against the FP64 oracle.
+ABI.  The records are the same arithmetic as the tape context's rebuilt ones
+on the same (plain chunked) route, so o, the final state and all eight
+gradients must equal that tape context's bit for bit; they are also checked
+against the FP64 oracle.
 """
 import numpy as np
 import pytest
@@ -19,7 +20,8 @@ def _run(inp, context):
     d = inp.to("cuda")
     o, fs, ctx = kda.recurrent_kda_training_forward(
         d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
-        cu_seqlens=d.cu_seqlens, cu_seqlens_cpu=inp.cu_seqlens, context=context)
+        cu_seqlens=d.cu_seqlens, cu_seqlens_cpu=inp.cu_seqlens, context=context,
+        route=kda.ROUTE_CHUNK)
     grads = kda.recurrent_kda_training_backward(ctx, d.do, d.dfinal_state)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), fs.cpu().numpy(), [g.float().cpu().numpy() for g in grads]
