@@ -110,16 +110,19 @@ typedef enum {
                                 (P, Q and P transposed, which the backward chains
                                 with).
                                 AUTO takes it when 2 x segments x Hv <= 768 and the
-                                longest sequence spans 4 or more tape segments.  Without
+                                longest sequence spans more than 4 tape segments (4 or
+                                more when KDA_ROUTE_CHUNK_SPLIT does not apply).  Without
                                 a context the plain chunked kernel runs. */
-    KDA_ROUTE_CHUNK_SPLIT = 4 /* training forward (tape context or none): the chunked kernel
+    KDA_ROUTE_CHUNK_SPLIT = 4 /* training forward (tape context or none): the chunk form
                                 with each task's 128 value columns split over two
-                                workgroups.  The state path is column-local, so each half
-                                runs on its own and repeats the state-independent work
-                                (prologue, 16x16 algebra); with fewer tasks than compute
-                                units this shortens each task's chain.  Same tape and
-                                backward as KDA_ROUTE_CHUNK.  AUTO takes it when
-                                2 x tasks <= 256 and route 3 is not taken. */
+                                workgroups (the state path is column-local).  In each,
+                                four waves run the state path while four others prepare
+                                the next four chunks' state-independent work (prologue,
+                                16x16 algebra), so with fewer tasks than compute units
+                                a task's chain of chunks is shorter.  Its tape equals
+                                KDA_ROUTE_CHUNK's to rounding; same backward.  AUTO
+                                takes it when 2 x tasks <= 256 and route 3 is not
+                                taken. */
 } kda_route;
 
 /* What the training forward saves for the backward.  TAPE: the FP32 state
