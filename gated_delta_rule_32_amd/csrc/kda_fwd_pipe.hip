@@ -132,6 +132,9 @@ __global__ __launch_bounds__(PP_THREADS, 1) void fwd_pipe_kernel(FwdArgs a) {
 
     if (prod) {
         // ================= producer j: chunks j, j+4, ... =================
+        // (issue priority over the consumer on the same SIMD: the producers
+        // set the step, the consumers have slack in it)
+        __builtin_amdgcn_s_setprio(3);
         const int j = wave - 4;
         const int lane = tid & 63;
         const int gq = lane >> 4;
