@@ -505,6 +505,9 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         };
         float rq_next, rk_next;
         if (wave == 0) {
+            // the substitution is the phase's longest chain: top issue
+            // priority until the next chunk resets it
+            __builtin_amdgcn_s_setprio(3);
             SolveScratch& ws = sm.sv;
             f32x4 akk = zero4();
             if (precise) {   // Kg_hi Ki_hi + Kg_hi Ki_lo + Kg_lo Ki_hi
