@@ -8,7 +8,9 @@ the whole tensors span 2.31e9 (past it): the second sequence's rows, and the
 records, tape and states of its last heads, are reachable only through the
 64-bit bases.  Forward (o, final state) and backward (all eight gradients) of
 tasks at both ends are compared with the FP64 oracle, each task on its own
-(its inputs copied back from the device).
+(its inputs copied back from the device).  The forward runs again on the
+column-split route (whose kernel addresses rows the same way) and is checked
+at the same tasks.
 
 Inputs are drawn on the device from a seeded generator with the workloads'
 distributions (drawing 4.6 GB tensors on the host would take minutes); the
@@ -54,6 +56,9 @@ def test_offsets_past_2_31():
         d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
         cu_seqlens=d.cu_seqlens, cu_seqlens_cpu=d.extra["cu_seqlens_cpu"])
     grads = kda.recurrent_kda_training_backward(ctx, d.do, d.dfinal_state)
+    o4, fs4, _ = kda.recurrent_kda_training_forward(
+        d.q, d.k, d.v, d.g, d.beta, d.A_log, d.dt_bias, d.initial_state,
+        cu_seqlens=d.cu_seqlens, cu_seqlens_cpu=d.extra["cu_seqlens_cpu"], route=kda.ROUTE_CHUNK_SPLIT)
     torch.cuda.synchronize()
     print("  device work done", flush=True)
     for (n, h) in ((1, H - 1), (0, 3)):
@@ -63,6 +68,8 @@ def test_offsets_past_2_31():
         got_o = o[:, sl, h:h + 1].float().cpu().numpy()
         pu.report_and_check([("o", got_o, ref_o)])
         pu.assert_state_close("final_state", fs[n:n + 1, h:h + 1].cpu().numpy(), ref_s)
+        pu.report_and_check([("o (column split)", o4[:, sl, h:h + 1].float().cpu().numpy(), ref_o)])
+        pu.assert_state_close("final_state (column split)", fs4[n:n + 1, h:h + 1].cpu().numpy(), ref_s)
         ref_g = pu.oracle_backward(inp)
         dq, dk, dv, dg, dbeta, dA, ddt, dS0 = grads
         got = [dq[:, sl, h:h + 1], dk[:, sl, h:h + 1], dv[:, sl, h:h + 1], dg[:, sl, h:h + 1],
@@ -72,5 +79,5 @@ def test_offsets_past_2_31():
         print(f"  task (n={n}, h={h})", flush=True)
         pu.report_and_check(pairs)
         assert np.isfinite(got_o).all()
-    del o, fs, ctx, grads, d
+    del o, fs, ctx, grads, d, o4, fs4
     torch.cuda.empty_cache()
