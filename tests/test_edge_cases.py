@@ -10,7 +10,7 @@ C ABI, forward and backward against the FP64 oracle:
 * beta -> 1 (the delta rule recalls v exactly) and beta -> 0 (pure decay);
 * zero values and zero initial state (output and final state exactly zero);
 * eight value heads per q/k head;
-* one long sequence (a single task) on both routes;
+* one long sequence (a single task) on the chunked, row-split and column-split routes;
 * sequence lengths on and around the tape interval.
 
 Inputs are the seeded draws of the workload generator with the named tensors
@@ -124,13 +124,15 @@ def test_full_precision_on_workload(name):
         pu.assert_state_close(f"final_state[{n},{h}]", fs[n, h], ref_s[n, h])
 
 
-@pytest.mark.parametrize("route", [1, 2], ids=["fwd-chunk", "fwd-rowsplit"])
+# after a route-3 forward the backward is the segment-parallel one (the dS
+# chain through each 64-token segment's affine map)
+@pytest.mark.parametrize("route", [1, 2, 3, 4], ids=["fwd-chunk", "fwd-rowsplit", "fwd-segments", "fwd-split"])
 @pytest.mark.parametrize("case", list(CASES.keys()))
 def test_backward_edge(case, route):
     problem, seed, set_to = CASES[case]
     inp = _inputs(problem, seed, **set_to)
     print(f"[edge bwd] case={case} fwd-route={route} lengths={problem.lengths}", flush=True)
-    got = pu.run_backward(inp, route=route)
+    got = pu.run_backward(inp, route=route, ckpt=64 if route == 3 else 0)
     ref = pu.oracle_backward(inp)
     pu.report_and_check(list(zip(pu.GRAD_NAMES, got, ref)))
 
