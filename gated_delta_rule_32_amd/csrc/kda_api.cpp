@@ -61,7 +61,7 @@ struct Prob {
     int64_t tokens;              // B * T
     int64_t num_tasks;
     int64_t total_ck;            // stored checkpoints (sum ceil(L/ck) - 1)
-    int64_t total_chunks;        // sum ceil(L/16)
+    int64_t total_chunks;        // sum ceil(L/16), each rounded up to even (record count)
     int64_t total_segs;          // sum ceil(L/ck)
     int64_t max_len;             // longest sequence
 };
@@ -171,7 +171,7 @@ kda_status validate(const kda_problem* p, Prob& out) {
         out.max_len = std::max(out.max_len, L);
         out.total_ck += (L + ck - 1) / ck - 1;
         out.total_segs += (L + ck - 1) / ck;
-        out.total_chunks += (L + kChunk - 1) / kChunk;
+        out.total_chunks += ((L + kChunk - 1) / kChunk + 1) & ~(int64_t)1;
     }
     // kernels address a sequence's rows with 32-bit element offsets
     for (int64_t L : out.len)
@@ -244,7 +244,7 @@ void fill_plan(const Prob& p, const PlanLayout& l, char* h) {
         st[n] = p.start[n];
         ln[n] = (int32_t)p.len[n];
         to[n + 1] = to[n] + (p.len[n] + p.ck - 1) / p.ck - 1;
-        co[n + 1] = co[n] + (p.len[n] + kChunk - 1) / kChunk;
+        co[n + 1] = co[n] + (((p.len[n] + kChunk - 1) / kChunk + 1) & ~(int64_t)1);  // even
     }
     for (int n : seq_order(p)) {
         const int64_t nseg = (p.len[n] + p.ck - 1) / p.ck;
@@ -458,17 +458,30 @@ constexpr size_t kMaxCtx = 4096;
 size_t tape_bytes(const Prob& p) {
     return (size_t)p.total_ck * (size_t)p.Hv * (size_t)kStateElems * sizeof(float);
 }
-// per (16-token chunk, value head) record: BF16 chunk-start state frags,
-// BF16 RF(U), FP32 T^T, Akk^T and scale*Aqk
-constexpr size_t kRecS0 = (size_t)kStateElems * 2, kRecU = (size_t)kChunk * D * 2,
-                 kRecTA = (size_t)3 * kChunk * kChunk * sizeof(float);
+// Records per (16-token chunk, value head): BF16 RF(U), FP32 T^T, Akk^T and
+// scale*Aqk; and the BF16 chunk-start state frags, either per chunk or, with
+// pair records, per (pair of chunks, value head) for the even chunk only,
+// with its BF16 CF(U), CF(Kt) and FP32 exp(gC), which step that state to the
+// odd chunk.  `recs` counts chunk records (an even number per sequence and
+// head).
+constexpr size_t kRecS0 = (size_t)kStateElems * 2, kRecX = (size_t)kda::REC_X_ELEMS * 2,
+                 kRecU = (size_t)kChunk * D * 2, kRecTA = (size_t)3 * kChunk * kChunk * sizeof(float);
 struct RecLayout {
-    size_t s0, u, ta, end;  // byte offsets of the three record arrays
+    size_t s0, x, u, ta, end;  // byte offsets of the four record arrays
 };
-RecLayout rec_layout(size_t recs, size_t base) {
+// Pair records (the start state of even chunks only) when the adjoint has
+// tasks enough to hide forming the odd chunks' states: measured with 768
+// tasks (8 x 1024 tokens, 96 heads) the backward is 2.7% faster with them
+// (the rebuild writes 30% fewer bytes), with 128 tasks (4 x 4096 tokens, 32
+// value heads), where each task runs at the latency of its chain, 3.5% slower.
+// (The segment-parallel route, for few tasks, keeps a start state per chunk.)
+constexpr int64_t kPairMinTasks = 256;
+bool rec_pairs(const Prob& p) { return p.num_tasks > kPairMinTasks && p.route != 3; }
+RecLayout rec_layout(size_t recs, size_t base, bool pairs) {
     RecLayout r;
     r.s0 = base;
-    r.u = align256(r.s0 + recs * kRecS0);
+    r.x = align256(r.s0 + (pairs ? recs / 2 : recs) * kRecS0);
+    r.u = align256(r.x + (pairs ? recs / 2 : 0) * kRecX);
     r.ta = align256(r.u + recs * kRecU);
     r.end = align256(r.ta + recs * kRecTA);
     return r;
@@ -477,7 +490,7 @@ RecLayout rec_layout(size_t recs, size_t base) {
 size_t seg_scratch_off(const Prob& p) { return align256(256 + tape_bytes(p)); }
 size_t ctx_bytes_for(const Prob& p) {
     if (p.ctxmode == KDA_CONTEXT_RECORDS)
-        return rec_layout((size_t)p.total_chunks * p.Hv, 256).end;
+        return rec_layout((size_t)p.total_chunks * p.Hv, 256, rec_pairs(p)).end;
     if (p.route == 3)
         return seg_scratch_off(p) + 3 * (size_t)p.total_segs * p.Hv * (size_t)kStateElems * sizeof(float);
     return 256 + tape_bytes(p);
@@ -532,6 +545,7 @@ kda::FwdArgs make_fwd_args(const Prob& p, const kda::DevPlan& plan, const void* 
     a.ck_every = p.ck;
     a.scale = p.scale;
     // log2-domain decay sum above which a chunk runs precise: ln(exp(-2))
+    a.rec_pairs = rec_pairs(p) ? 1 : 0;
     a.precise_log2 = p.precision == KDA_PRECISION_FULL   ? -INFINITY
                      : p.precision == KDA_PRECISION_FAST ? 1.0f
                                                          : -2.0f * 1.4426950408889634f;
@@ -575,18 +589,19 @@ kda_status kda_fwd_ctx_bytes(const kda_problem* pp, size_t* bytes) {
     return KDA_OK;
 }
 
-// Backward workspace: the rebuild's per-chunk records (BF16 chunk-start
-// state, BF16 U, FP32 T^T / Akk^T / Aqk), then FP32 dq/dk partials when value
-// heads share a q/k head, then per-task parameter-gradient partials.
+// Backward workspace: the rebuild's records (rec_layout), then BF16 dq/dk
+// partials when value heads share a q/k head, then per-task parameter-gradient
+// partials.
 struct WsLayout {
-    size_t s0, u, ta, dqk, par, seg_r, seg_e, total;
+    size_t s0, x, u, ta, dqk, par, seg_r, seg_e, total;
 };
 static WsLayout ws_layout(const Prob& p) {
     WsLayout w;
     // the rebuilt chunk records (none when the context already holds them)
     const size_t recs = p.ctxmode == KDA_CONTEXT_RECORDS ? 0 : (size_t)p.total_chunks * p.Hv;
-    const RecLayout r = rec_layout(recs, 0);
+    const RecLayout r = rec_layout(recs, 0, rec_pairs(p));
     w.s0 = r.s0;
+    w.x = r.x;
     w.u = r.u;
     w.ta = r.ta;
     size_t off = r.end;
@@ -668,8 +683,9 @@ kda_status fwd_launch(const Prob& p, int dev, const void* plan_dev, const PlanLa
     a.s_final = final_state;
     a.tape = nullptr;
     if (ctx != nullptr && p.ctxmode == KDA_CONTEXT_RECORDS) {
-        const RecLayout r = rec_layout((size_t)p.total_chunks * p.Hv, 256);
+        const RecLayout r = rec_layout((size_t)p.total_chunks * p.Hv, 256, rec_pairs(p));
         a.rec_s0 = (kda::bf16_t*)((char*)ctx + r.s0);
+        a.rec_x = (kda::bf16_t*)((char*)ctx + r.x);
         a.rec_u = (kda::bf16_t*)((char*)ctx + r.u);
         a.rec_ta = (float*)((char*)ctx + r.ta);
     } else if (ctx != nullptr) {
@@ -839,13 +855,15 @@ kda_status kda_bwd(const kda_problem* pp, const void* q, const void* k, const vo
     char* ws = (char*)workspace;
     const bool records = p.ctxmode == KDA_CONTEXT_RECORDS;
     if (records) {  // the forward stored every chunk's records in the context
-        const RecLayout r = rec_layout((size_t)p.total_chunks * p.Hv, 256);
+        const RecLayout r = rec_layout((size_t)p.total_chunks * p.Hv, 256, rec_pairs(p));
         b.f.rec_s0 = (kda::bf16_t*)((char*)ctx + r.s0);
+        b.f.rec_x = (kda::bf16_t*)((char*)ctx + r.x);
         b.f.rec_u = (kda::bf16_t*)((char*)ctx + r.u);
         b.f.rec_ta = (float*)((char*)ctx + r.ta);
     } else {        // rebuilt from the tape into the workspace
         b.f.tape = (float*)((char*)ctx + 256);
         b.f.rec_s0 = (kda::bf16_t*)(ws + wl.s0);
+        b.f.rec_x = (kda::bf16_t*)(ws + wl.x);
         b.f.rec_u = (kda::bf16_t*)(ws + wl.u);
         b.f.rec_ta = (float*)(ws + wl.ta);
     }

@@ -52,8 +52,11 @@ namespace {
 constexpr int BW_THREADS = 256;
 constexpr float LN2 = 0.6931471805599453f;
 
-// Record layouts (per record = (chunk, value head)); see the state rebuild.
-constexpr int REC_S0 = D * D;       // bf16: [8 kb][8 vb][64 lanes][4]
+// Record layouts (per record = (chunk, value head); per pair record =
+// (pair of chunks 2p, 2p+1, value head)); see the state rebuild.
+constexpr int REC_S0 = D * D;       // bf16 per pair: [8 kb][8 vb][64 lanes][4], chunk 2p's S0
+constexpr int REC_X = REC_X_ELEMS;  // bf16 per pair: CF(U) [8 vb][64][4], CF(Kt) [8 kb][64][4]
+                                    // of chunk 2p, then exp(gC) [128] as FP32
 constexpr int REC_U = CH * D;       // bf16: [8 vb][64 lanes][4], RF(U)
 constexpr int REC_TA = 3 * CH * CH; // f32:  T^T, Akk^T, Aqk'
 
@@ -121,8 +124,10 @@ __device__ __forceinline__ f32x4 mma16_split(bf16x4 ah, bf16x4 al, bf16x4 bh, bf
 }  // namespace
 
 // kSeg: the segment-parallel passes (b.seg_pass 1 or 2), a separate instance
-// so that the whole-task one keeps its code.
-template <bool kSeg>
+// so that the whole-task one keeps its code.  kPairs: pair records (the
+// start states of even chunks only; b.f.rec_pairs), also an instance of its
+// own, since forming the odd chunks' states costs the other one registers.
+template <bool kSeg, bool kPairs>
 __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
     __shared__ BwdLds sm;
     const FwdArgs& a = b.f;
@@ -276,6 +281,11 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         const bool valid_r = !kTail || r < nv;
         const bool valid_c = !kTail || cl < nv;
         const int64_t rec = (rec0 + ci) * a.Hv + h;
+        // with pair records (chunks 2p, 2p+1; rec0 is even) the pair holds
+        // chunk 2p's start state, and an odd chunk steps it forward by chunk
+        // 2p's update; otherwise every chunk holds its own
+        const int64_t prec = kPairs ? ((rec0 + ci) >> 1) * a.Hv + h : rec;
+        const bool odd = kPairs && (ci & 1) != 0;
         const int kb0 = 2 * wave;
 
         // Global operands of the state-side products, issued in the prologue
@@ -295,12 +305,25 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         // hold back the in-order issue of later work).  The chunk's P1 ran in
         // the previous chunk's last phase; its barrier published it.
         {
-            const bf16* s0p = (const bf16*)a.rec_s0 + rec * REC_S0;  // uniform record base
+            const bf16* s0p = (const bf16*)a.rec_s0 + prec * REC_S0;  // uniform record base
 #pragma unroll
             for (int vb = 0; vb < 8; ++vb)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     s0f[vb][j] = *(const bf16x4*)at(s0p, ((kb0 + j) * 8 + vb) * 256 + lane * 4);
+        }
+        // odd chunk: chunk 2p's CF(U), this wave's CF(Kt) blocks and exp(gC)
+        bf16x4 xu[8], xk[2];
+        float xg[2];
+        if (odd) {
+            const bf16* xp = (const bf16*)a.rec_x + prec * REC_X;
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb) xu[vb] = *(const bf16x4*)at(xp, vb * 256 + lane * 4);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                xk[j] = *(const bf16x4*)at(xp, 2048 + (kb0 + j) * 256 + lane * 4);
+                xg[j] = *(const float*)at(xp, 4096 + 2 * (16 * (kb0 + j) + cl));
+            }
         }
         // ---- P2: prefix sums over the chunk's tokens.  Every wave takes 32
         // channels: lanes 0-31 sum rows 0-7, lanes 32-63 rows 8-15 and add the
@@ -384,6 +407,30 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         if (tix < REC_TA / 4) ((float4*)&sm.ta[0][0][0])[tix] = ta4;
         // the row inputs are dead: fetch the previous chunk's
         load_row(cur, max(t0 - CH + r, 0), c8);
+        // odd chunk: its start state from chunk 2p's, S0 = S0(2p)
+        // diag(exp(gC(2p))) + U(2p)^T Kt(2p), frag by frag in the layout of s0f
+        // (A = CF(U) frag vb, B = CF(Kt) block kb0 + j); after the prologue,
+        // so that its loads have arrived
+        if (odd) {
+#pragma unroll
+            for (int vg = 0; vg < 8; vg += 2) {
+                f32x4 c[2][2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) c[e][j][i] = (float)s0f[vg + e][j][i] * xg[j];
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) c[e][j] = mma16(xu[vg + e], xk[j], c[e][j]);
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) s0f[vg + e][j] = to_bf4(c[e][j]);
+            }
+        }
         __syncthreads();
 
         // ---- M1 (per wave): state-side products with the incoming dS ----
@@ -787,7 +834,12 @@ __global__ void bwd_dqk_reduce_kernel(BwdArgs b, int64_t items) {
 
 hipError_t launch_bwd_chunk(const BwdArgs& b, hipStream_t s) {
     if (b.f.num_tasks == 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_chunk_kernel<false>, dim3((unsigned)b.f.num_tasks), dim3(BW_THREADS), 0, s, b);
+    if (b.f.rec_pairs)
+        hipLaunchKernelGGL((bwd_chunk_kernel<false, true>), dim3((unsigned)b.f.num_tasks), dim3(BW_THREADS), 0,
+                           s, b);
+    else
+        hipLaunchKernelGGL((bwd_chunk_kernel<false, false>), dim3((unsigned)b.f.num_tasks), dim3(BW_THREADS), 0,
+                           s, b);
     return hipGetLastError();
 }
 
@@ -854,7 +906,7 @@ hipError_t launch_bwd_segments(const BwdArgs& b, int N, hipStream_t s) {
     if (b.f.seg_items == 0) return hipSuccess;
     BwdArgs p1 = b;
     p1.seg_pass = 1;
-    hipLaunchKernelGGL(bwd_chunk_kernel<true>, dim3((unsigned)b.f.seg_items), dim3(BW_THREADS), 0, s, p1);
+    hipLaunchKernelGGL((bwd_chunk_kernel<true, false>), dim3((unsigned)b.f.seg_items), dim3(BW_THREADS), 0, s, p1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(seg_combine_bwd_kernel, dim3((unsigned)(N * b.f.Hv * 8)), dim3(256), 0, s, b);
@@ -862,7 +914,7 @@ hipError_t launch_bwd_segments(const BwdArgs& b, int N, hipStream_t s) {
     if (e != hipSuccess) return e;
     BwdArgs p2 = b;
     p2.seg_pass = 2;
-    hipLaunchKernelGGL(bwd_chunk_kernel<true>, dim3((unsigned)b.f.seg_items), dim3(BW_THREADS), 0, s, p2);
+    hipLaunchKernelGGL((bwd_chunk_kernel<true, false>), dim3((unsigned)b.f.seg_items), dim3(BW_THREADS), 0, s, p2);
     return hipGetLastError();
 }
 

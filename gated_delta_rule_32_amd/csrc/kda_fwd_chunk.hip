@@ -99,6 +99,9 @@ struct FwdLds {
 // above -5 (so that the factors exp(+-gc) stay in range), so the host sends
 // only the in-kernel gate with lower_bound >= -5 here; log-space gates run
 // token by token.
+// kFwdRebuildPairs and kFwdRecordsPairs store the records with the
+// chunk-start state of even chunks only, and with what steps it to the odd
+// chunk after (pair records, for calls with many tasks).
 // kFwdInferCkpt is the same with state checkpoints (a separate instance, so
 // that the plain one keeps its registers).  kFwdSegPQ and kFwdSegOut make the
 // segment-parallel training forward for calls with few tasks: each tape
@@ -108,16 +111,17 @@ struct FwdLds {
 // segments into the tape, and kFwdSegOut reruns every segment from its tape
 // state for o and the final state.
 constexpr int kFwdTape = 0, kFwdRebuild = 1, kFwdRecords = 2, kFwdInfer = 3, kFwdInferCkpt = 4,
-              kFwdSegPQ = 5, kFwdSegOut = 6;
+              kFwdSegPQ = 5, kFwdSegOut = 6, kFwdRebuildPairs = 7, kFwdRecordsPairs = 8;
 
 template <int kMode>
 __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     constexpr int kNVB = 2;  // 16-column blocks per wave
-    constexpr bool kRebuild = kMode == kFwdRebuild;  // one segment, no output
+    constexpr bool kPairs = kMode == kFwdRebuildPairs || kMode == kFwdRecordsPairs;  // pair records
+    constexpr bool kRebuild = kMode == kFwdRebuild || kMode == kFwdRebuildPairs;  // one segment, no output
     constexpr bool kSegPQ = kMode == kFwdSegPQ;
     constexpr bool kSegTask = kRebuild || kSegPQ || kMode == kFwdSegOut;  // one tape segment per task
     constexpr bool kOut = !kRebuild && !kSegPQ;      // o and the final state
-    constexpr bool kRec = kMode == kFwdRebuild || kMode == kFwdRecords;  // per-chunk records
+    constexpr bool kRec = kRebuild || kMode == kFwdRecords || kMode == kFwdRecordsPairs;  // records
     constexpr bool kInfer = kMode == kFwdInfer || kMode == kFwdInferCkpt;  // BF16 pool state, options
     constexpr bool kCkpt = kMode == kFwdInferCkpt;   // state checkpoints
     __shared__ FwdLds sm;
@@ -329,7 +333,14 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         // the last one finishes alone; raising the priority of those with
         // more chunks left keeps co-resident tasks abreast.
         set_prio_by_remaining(ce - ci, ce - cb);
-        const int64_t rec = (rec0 + ci) * a.Hv + h;  // record index (rebuild only)
+        const int64_t rec = (rec0 + ci) * a.Hv + h;  // record index (records only)
+        // with pair records (chunks 2p, 2p+1; rec0 is even) the even chunk
+        // stores its start state and what steps it to the odd one (CF(U),
+        // CF(Kt), exp(gC)), from which the adjoint forms the odd chunk's
+        // start state; otherwise every chunk stores its start state
+        const int64_t prec = kPairs ? ((rec0 + ci) >> 1) * a.Hv + h : rec;
+        const bool rec_even = !kPairs || (ci & 1) == 0;   // stores S0
+        const bool rec_step = kPairs && (ci & 1) == 0;    // stores the step
         if constexpr (kCkpt) {
             // state checkpoint before token t0 (E is a multiple of the chunk)
             // (the row comes from the caller's device copy of the starts, which
@@ -410,8 +421,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                 *(bf16x4*)&sm.rf_kg[orf + 64 * s] = kg4[s];
                 *(bf16x4*)&sm.rf_ki[orf + 64 * s] = ki4[s];
             }
-            // CF(Kt) hi / lo pairs (BF16 in precise chunks, FP16 in the
-            // others): lane slot (gq, k) holds the hi parts of tokens
+            // CF(Kt) hi / lo FP16 pairs: lane slot (gq, k) holds the hi parts of tokens
             // 4gq..4gq+3, then their lo parts; channel c8 + j of row r sits 8j
             // elements after channel c8 (one 16-channel block)
             const int ocf = (c8 >> 4) * FS2 + (((r >> 2) << 4) + (c8 & 15)) * 8 + (r & 3);
@@ -453,13 +463,15 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
                     for (int vb = 0; vb < kNVB; ++vb) {
                         if constexpr (kRec) {
-                            const bf16x4 ident = identity_frag(lane);
-                            const int vbg = vb0 + vb;
-                            bf16* dst = (bf16*)a.rec_s0 + rec * (D * D) + lane * 4;
-                            *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) =
-                                to_bf4(transpose_frag(to_bf4(S[2 * j][vb]), ident));
-                            *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) =
-                                to_bf4(transpose_frag(to_bf4(S[2 * j + 1][vb]), ident));
+                            if (rec_even) {
+                                const bf16x4 ident = identity_frag(lane);
+                                const int vbg = vb0 + vb;
+                                bf16* dst = (bf16*)a.rec_s0 + prec * (D * D) + lane * 4;
+                                *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) =
+                                    to_bf4(transpose_frag(to_bf4(S[2 * j][vb]), ident));
+                                *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) =
+                                    to_bf4(transpose_frag(to_bf4(S[2 * j + 1][vb]), ident));
+                            }
                         }
                         bf16x4 h0, l0, h1, l1;
                         split4(S[2 * j][vb], h0, l0);
@@ -484,13 +496,15 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
                     sb[j][vb] = cat8(s0, s1);
                     Y[vb] = mma32(kg8, sb[j][vb], Y[vb]);    // lane (gq, v) holds Y[4gq+i][v]
                     if constexpr (kRec) {
-                        // chunk-start state record: frag (kb, vb) with lane (gq, k)
-                        // holding S0[16vb + 4gq + i][16kb + k]
-                        const bf16x4 ident = identity_frag(lane);
-                        const int vbg = vb0 + vb;
-                        bf16* dst = (bf16*)a.rec_s0 + rec * (D * D) + lane * 4;
-                        *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) = to_bf4(transpose_frag(s0, ident));
-                        *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) = to_bf4(transpose_frag(s1, ident));
+                        // chunk-start state record (even chunks): frag (kb, vb)
+                        // with lane (gq, k) holding S0[16vb + 4gq + i][16kb + k]
+                        if (rec_even) {
+                            const bf16x4 ident = identity_frag(lane);
+                            const int vbg = vb0 + vb;
+                            bf16* dst = (bf16*)a.rec_s0 + prec * (D * D) + lane * 4;
+                            *(bf16x4*)(dst + ((2 * j) * 8 + vbg) * 256) = to_bf4(transpose_frag(s0, ident));
+                            *(bf16x4*)(dst + ((2 * j + 1) * 8 + vbg) * 256) = to_bf4(transpose_frag(s1, ident));
+                        }
                     }
                 }
             }
@@ -648,8 +662,11 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         auto out_term = [&](int vb, bf16x4 uh) __attribute__((always_inline)) {
             if constexpr (kRec) {
                 // U record, RF layout: lane (gq, c) holds U[c][16vb + 4gq + i]
-                const bf16x4 ut = to_bf4(transpose_frag(to_bf4(U[vb]), identity_frag(lane)));
+                const bf16x4 ub = to_bf4(U[vb]);
+                const bf16x4 ut = to_bf4(transpose_frag(ub, identity_frag(lane)));
                 *(bf16x4*)at((bf16*)a.rec_u + rec * (CH * D), ((vb0 + vb) * 64 + lane) * 4) = ut;
+                // even chunks: CF(U) as well (lane (gq, c) holds U[4gq + i][16vb + c])
+                if (rec_step) *(bf16x4*)((bf16*)a.rec_x + prec * REC_X_ELEMS + ((vb0 + vb) * 64 + lane) * 4) = ub;
             }
             if constexpr (kOut) {
                 // [U_hi|U_hi] against [Aqk/2;Aqk/2]: the chain's last step is a
@@ -738,6 +755,24 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
 #pragma unroll
                 for (int vb = 0; vb < kNVB; ++vb) S[kb][vb] *= isc;
         }
+        if constexpr (kRec) {
+            // even chunks of pair records: this wave's CF(Kt) blocks vb0,
+            // vb0 + 1 in BF16 (hi + lo of the FP16 pair) and, from wave 0, exp(gC)
+            if (rec_step) {
+                bf16* xp = (bf16*)a.rec_x + prec * REC_X_ELEMS;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int kb = vb0 + j;
+                    const f16x8 t2 = *(const f16x8*)&sm.cf_kt[kb * FS2 + lane * 8];
+                    f32x4 kt;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) kt[i] = (float)t2[i] + (float)t2[i + 4];
+                    *(bf16x4*)(xp + 2048 + (kb * 64 + lane) * 4) = to_bf4(kt);
+                }
+                if (vb0 == 0)
+                    *(float2*)((float*)(xp + 4096) + 2 * lane) = *(const float2*)&sm.gamc[ci & 1][2 * lane];
+            }
+        }
         const int tend = t0 + nv;
         if (kMode == kFwdTape && a.tape != nullptr && tend < L && (tend % a.ck_every) == 0) {
             const int64_t jck = tend / a.ck_every;
@@ -790,6 +825,9 @@ hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s) {
     else if (a.infer)
         hipLaunchKernelGGL(fwd_chunk_kernel<kFwdInfer>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0,
                            s, a);
+    else if (a.rec_s0 != nullptr && a.rec_pairs)
+        hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRecordsPairs>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS),
+                           0, s, a);
     else if (a.rec_s0 != nullptr)
         hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRecords>, dim3((unsigned)a.num_tasks), dim3(FC_THREADS), 0,
                            s, a);
@@ -804,7 +842,12 @@ hipError_t launch_fwd_chunk(const FwdArgs& a, hipStream_t s) {
 // One workgroup per (tape segment, value head): num_items = segments * Hv.
 hipError_t launch_state_rebuild(const FwdArgs& a, int64_t num_items, hipStream_t s) {
     if (num_items == 0) return hipSuccess;
-    hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRebuild>, dim3((unsigned)num_items), dim3(FC_THREADS), 0, s, a);
+    if (a.rec_pairs)
+        hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRebuildPairs>, dim3((unsigned)num_items), dim3(FC_THREADS), 0,
+                           s, a);
+    else
+        hipLaunchKernelGGL(fwd_chunk_kernel<kFwdRebuild>, dim3((unsigned)num_items), dim3(FC_THREADS), 0, s,
+                           a);
     return hipGetLastError();
 }
 

@@ -8,12 +8,17 @@ namespace kda {
 
 typedef unsigned short bf16_t;  // BF16 bits in memory
 
+// 16-bit elements of one pair record of rec_x: CF(U) and CF(Kt) of the pair's
+// even chunk (2048 BF16 each), then exp(gC) (128 FP32).
+constexpr int REC_X_ELEMS = 2 * 2048 + 2 * 128;
+
 // Device-side schedule built on the host from the sequence lengths.  Task i
 // (0 <= i < num_tasks, longest sequence first) is (n, h) = (task[i] / Hv,
 // task[i] % Hv).  Sequence n occupies flattened tokens [seq_start[n],
 // seq_start[n] + seq_len[n]) of the [B*T] token axis.  tape_off[n] counts the
 // stored checkpoints of the sequences before n (ceil(L/C_ck) - 1 each) and
-// chunk_off[n] the 16-token chunks (ceil(L/16) each).
+// chunk_off[n] the 16-token chunks (ceil(L/16) each, rounded up to even, so
+// that every sequence's chunk pairs start at an even index).
 struct DevPlan {
     const int32_t* task;
     const int64_t* seq_start;
@@ -34,11 +39,17 @@ struct FwdArgs {
     void* o;
     float* s_final;         // [N][Hv][128][128]; may be null (state rebuild)
     float* tape;            // [ck][Hv][128][128]; may be null
-    // Per-chunk records written by the state rebuild and read by the adjoint,
-    // indexed by rec = (chunk_off[n] + chunk) * Hv + h (layouts: kda_bwd.hip).
-    bf16_t* rec_s0;         // [rec][8 kb][8 vb][64][4] chunk-start state, BF16
+    // Records written by the state rebuild and read by the adjoint (layouts:
+    // kda_bwd.hip).  Per chunk, rec = (chunk_off[n] + chunk) * Hv + h.  With
+    // rec_pairs the chunk-start state is stored for even chunks only, per
+    // pair of chunks (2p, 2p+1) at prec = ((chunk_off[n] + chunk) / 2) * Hv
+    // + h (chunk_off[n] is even), with what steps it to the odd chunk after;
+    // otherwise for every chunk, at prec = rec, and rec_x is unused.
+    bf16_t* rec_s0;         // [prec][8 kb][8 vb][64][4] chunk-start state, BF16
+    bf16_t* rec_x;          // [prec][REC_X] the even chunk's CF(U), CF(Kt) (BF16) and exp(gC) (FP32)
     bf16_t* rec_u;          // [rec][8 vb][64][4] U, BF16
     float* rec_ta;          // [rec][3][16][16] T^T, Akk^T, scale*Aqk
+    int rec_pairs;
     DevPlan plan;
     int Hqk, Hv, G;
     int num_tasks;

@@ -129,10 +129,13 @@ typedef enum {
  * every checkpoint_every tokens; the backward rebuilds each segment's chunk
  * states from it (small context, a rebuild pass in the backward).  RECORDS:
  * every chunk's start state (BF16), U (BF16) and T, Akk, Aqk (FP32), about
- * 39 KiB per 16 tokens and value head; the backward reruns no forward
- * recurrence (page "flashinfer.kda_training", paragraph 5), at the cost of a
- * larger context and a forward that writes it.  RECORDS needs the chunked
- * route. */
+ * 39 KiB per 16 tokens and value head; with more than 256 tasks (sequences
+ * x value heads; not on the segment-parallel route, which is for few tasks)
+ * the start state only of every other chunk, with what steps
+ * it to the next one (that chunk's U and Kt, BF16, and exp(gC)), about
+ * 27 KiB.  The backward reruns no forward recurrence (page
+ * "flashinfer.kda_training", paragraph 5), at the cost of a larger context
+ * and a forward that writes it.  RECORDS needs the chunked route. */
 typedef enum {
     KDA_CONTEXT_TAPE = 0,
     KDA_CONTEXT_RECORDS = 1
@@ -195,12 +198,13 @@ const char* kda_last_error(void);
 /* Bytes the forward context needs: with KDA_CONTEXT_TAPE the FP32 state tape
  * saved for the backward (one [Hv][128][128] slab per sequence and per
  * interval boundary strictly inside the sequence), with KDA_CONTEXT_RECORDS
- * one record per 16-token chunk and value head; plus alignment.  Validates
- * the problem. */
+ * the records of every 16-token chunk (an even number per sequence) and value
+ * head; plus alignment.  Validates the problem. */
 kda_status kda_fwd_ctx_bytes(const kda_problem* p, size_t* bytes);
 
 /* Bytes the backward workspace needs (with KDA_CONTEXT_TAPE the chunk
- * records rebuilt from the tape; FP32 partial sums).  Validates the problem. */
+ * records rebuilt from the tape; BF16 dq/dk partial sums when value heads
+ * share a q/k head; FP32 parameter partial sums).  Validates the problem. */
 kda_status kda_bwd_workspace_bytes(const kda_problem* p, size_t* bytes);
 
 /* Host planning only (no device access): the route the forward would take,

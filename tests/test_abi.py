@@ -96,10 +96,13 @@ def test_context_and_workspace_sizes():
     segs = 5 + 1 + 8
     assert kda.kda_fwd_ctx_bytes(p) == (256 + tape + 255) // 256 * 256 + 3 * segs * 2 * 128 * 128 * 4
     p.route = kda.ROUTE_CHUNK
-    chunks = sum((L + 15) // 16 for L in (300, 1, 511))
+    # chunk records per sequence, rounded up to even: 19 -> 20, 1 -> 2, 32
+    chunks = sum(((L + 15) // 16 + 1) // 2 * 2 for L in (300, 1, 511))
+    assert chunks == 54
     ws = kda.kda_bwd_workspace_bytes(p)
-    # per (chunk, value head): BF16 chunk-start state, BF16 U, FP32 T/Akk/Aqk;
-    # BF16 dq/dk partials per token and value head (G = 2); per-task partials
+    # per (chunk, value head): BF16 chunk-start state, BF16 U, FP32 T/Akk/Aqk
+    # (6 tasks: no pair records); BF16 dq/dk partials per token and value
+    # head (G = 2); per-task partials
     rec = 128 * 128 * 2 + 16 * 128 * 2 + 3 * 16 * 16 * 4
     tasks = 3 * 2
     need = chunks * 2 * rec + 812 * 2 * 2 * 128 * 2 + tasks * 2 * 128 * 4
@@ -196,21 +199,29 @@ def test_sequence_span_limit():
 
 
 def test_records_context_sizes_and_rejections():
-    """Per-chunk records context: one record per (16-token chunk, value head),
-    laid out as three arrays after a 256-byte header; the backward workspace
-    then holds no records."""
+    """Records context: one record per (16-token chunk, value head), each
+    sequence's chunks rounded up to an even count, after a 256-byte header;
+    with more than 256 tasks the chunk-start state only per (chunk pair,
+    value head), with the even chunk's column-layout U and Kt and exp(gC).
+    The backward workspace then holds no records."""
     cu = [0, 300, 301, 812]
+    chunks = sum(((L + 15) // 16 + 1) // 2 * 2 for L in (300, 1, 511))
+    per_chunk = 16 * 128 * 2 + 3 * 16 * 16 * 4          # U, T/Akk/Aqk
+    s0 = 128 * 128 * 2
+    step = 2 * 16 * 128 * 2 + 128 * 4                    # CF(U), CF(Kt), exp(gC)
+    for Hv, pairs in ((2, False), (96, True)):           # 6 and 288 tasks
+        p, keep = _packed(cu, Hqk=Hv // 2, Hv=Hv)
+        ws_tape = kda.kda_bwd_workspace_bytes(p)
+        p.context = kda.CONTEXT_RECORDS
+        recs = chunks * Hv
+        rec_bytes = recs * per_chunk + (recs // 2 * (s0 + step) if pairs else recs * s0)
+        ctx = kda.kda_fwd_ctx_bytes(p)
+        need = 256 + rec_bytes
+        assert need <= ctx <= need + 4 * 256
+        ws_rec = kda.kda_bwd_workspace_bytes(p)
+        assert ws_rec + rec_bytes <= ws_tape <= ws_rec + rec_bytes + 4 * 256
     p, keep = _packed(cu, Hqk=1, Hv=2)
-    ws_tape = kda.kda_bwd_workspace_bytes(p)
     p.context = kda.CONTEXT_RECORDS
-    chunks = sum((L + 15) // 16 for L in (300, 1, 511))
-    recs = chunks * 2
-    ctx = kda.kda_fwd_ctx_bytes(p)
-    need = 256 + recs * (128 * 128 * 2 + 16 * 128 * 2 + 3 * 16 * 16 * 4)
-    assert need <= ctx <= need + 3 * 256
-    ws_rec = kda.kda_bwd_workspace_bytes(p)
-    rec_bytes = recs * (128 * 128 * 2 + 16 * 128 * 2 + 3 * 16 * 16 * 4)
-    assert ws_rec + rec_bytes <= ws_tape <= ws_rec + rec_bytes + 3 * 256
     p.route = 2
     assert _status(kda.kda_fwd_ctx_bytes, p) == 11      # records need the chunked route
     p.route = 0

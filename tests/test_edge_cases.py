@@ -137,6 +137,32 @@ def test_backward_edge(case, route):
     pu.report_and_check(list(zip(pu.GRAD_NAMES, got, ref)))
 
 
+@pytest.mark.parametrize("case", ["no_decay", "weak_decay"])
+def test_backward_pair_records(case):
+    """More than 256 tasks (65 sequences of 1024 tokens x 4 value heads), so
+    the rebuild stores the start state of every other chunk only and the
+    adjoint forms the odd chunks' start states from their pairs; without
+    decay, and with weak decay, nothing forgets their rounding.  The
+    gradients of every value head of two sequences against the oracle (dq and
+    dk are then complete; dA_log and ddt_bias sum over every sequence and are
+    not compared here)."""
+    set_to = dict(g=-30.0, A_log=2.0) if case == "no_decay" else dict(g=-6.2, A_log=0.0, dt_bias=0.0)
+    problem = P([1024] * 65, 1, 4, packed=True)
+    inp = _inputs(problem, 213, **set_to)
+    print(f"[edge bwd] pair records, {case}, {problem.N * problem.Hv} tasks", flush=True)
+    got = pu.run_backward(inp, route=1)
+    tasks = [(n, h) for n in (0, 64) for h in range(problem.Hv)]
+    ref = pu.oracle_backward(inp, tasks=tasks)
+    m = pu.task_mask_tokens(problem, tasks)            # [B, T, Hv]
+    mt = m.any(axis=2)                                 # [B, T]
+    pairs = [("dq", got[0][mt], ref[0][mt]), ("dk", got[1][mt], ref[1][mt]),
+             ("dv", got[2][m], ref[2][m]), ("dg", got[3][m], ref[3][m]),
+             ("dbeta", got[4][m], ref[4][m])]
+    for (n, h) in tasks:
+        pairs.append((f"dinitial_state[{n},{h}]", got[7][n, h], ref[7][n, h]))
+    pu.report_and_check(pairs)
+
+
 @pytest.mark.parametrize("route", [1, 2, 4], ids=["chunk", "rowsplit", "split"])
 def test_long_single_sequence(route):
     """One 4096-token sequence and one head: a single task, 256 chunks in
