@@ -1,6 +1,6 @@
-"""GPU parity of the per-chunk records context (the forward stores every
-chunk's records, the backward reruns no forward recurrence), through the C
-ABI.  The records are the same arithmetic as the tape context's rebuilt ones
+"""GPU parity of the records context (the forward stores the chunks'
+records, the backward reruns no forward recurrence), through the C ABI, with
+a start state per chunk and, with more than 256 tasks, pair records.  The records are the same arithmetic as the tape context's rebuilt ones
 on the same (plain chunked) route, so o, the final state and all eight
 gradients must equal that tape context's bit for bit; they are also checked
 against the FP64 oracle.
@@ -32,6 +32,9 @@ CASES = {
     "ragged": (P([1, 15, 16, 17, 33, 100], 2, 4, packed=True), 300),
     "fixed3x80": (P([80] * 3, 2, 2, packed=False), 301),
     "long_segments": (P([600, 257], 1, 2, packed=True), 302),
+    # 258 tasks: pair records (the start state of every other chunk) in both
+    # contexts, odd-length sequences included
+    "pair_records": (P([300, 37] + [40] * 127, 1, 2, packed=True), 303),
 }
 
 
