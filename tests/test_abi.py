@@ -229,6 +229,35 @@ def test_records_context_sizes_and_rejections():
     assert _status(kda.kda_fwd_ctx_bytes, p) == 11      # unknown context kind
 
 
+def test_pair_records_threshold():
+    """Pair records (the start state of every other chunk) from 257 tasks on,
+    on the chunked routes; a start state per chunk up to 256 tasks and on the
+    segment-parallel route, for any task count."""
+    per_chunk = 16 * 128 * 2 + 3 * 16 * 16 * 4
+    s0 = 128 * 128 * 2
+    step = 2 * 16 * 128 * 2 + 128 * 4
+
+    def records(N, Hv, pairs, chunks=2):
+        recs = N * chunks * Hv
+        return recs * per_chunk + (recs // 2 * (s0 + step) if pairs else recs * s0)
+
+    for Hv, pairs in ((64, False), (128, True)):        # 4 x 64 = 256, 4 x 128 = 512 tasks
+        p = kda.make_problem(4, 32, Hv, Hv, 4, context=kda.CONTEXT_RECORDS, route=kda.ROUTE_CHUNK)
+        need = 256 + records(4, Hv, pairs)
+        assert need <= kda.kda_fwd_ctx_bytes(p) <= need + 4 * 256
+    # tape context with 512 tasks: the rebuilt records in the workspace are
+    # pair records on the chunked route (G = 1: no dq/dk partials; per-task
+    # parameter partials) ...
+    p1 = kda.make_problem(4, 32, 128, 128, 4, route=kda.ROUTE_CHUNK)
+    need = records(4, 128, True) + 512 * 2 * 128 * 4
+    assert need <= kda.kda_bwd_workspace_bytes(p1) <= need + 8 * 256
+    # ... and a start state per chunk on the segment-parallel route (16-token
+    # segments: 8 segments x 128 heads of parameter partials, R and dS_end)
+    p3 = kda.make_problem(4, 32, 128, 128, 4, route=kda.ROUTE_SEGMENTS, checkpoint_every=16)
+    need = records(4, 128, False) + 1024 * 2 * 128 * 4 + 2 * 1024 * 128 * 128 * 4
+    assert need <= kda.kda_bwd_workspace_bytes(p3) <= need + 8 * 256
+
+
 def test_status_strings_cover_every_code():
     hdr = open(os.path.join(ROOT, "include", "libkda.h")).read()
     codes = {name: int(val) for name, val in re.findall(r"\b(KDA_(?:OK|ERR_[A-Z_]+))\s*=\s*(\d+)", hdr)}
