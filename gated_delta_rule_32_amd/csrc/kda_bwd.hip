@@ -144,7 +144,7 @@ __global__ __launch_bounds__(BW_THREADS, 2) void bwd_chunk_kernel(BwdArgs b) {
         segidx = a.plan.tape_off[n] + n + seg;
         code = (int)segidx * a.Hv + h;  // parameter-partial slot
     } else {
-        code = a.plan.task[blockIdx.x];
+        code = a.plan.task[xcd_order(blockIdx.x, a.num_tasks, a.G)];
         n = code / a.Hv;
         h = code - n * a.Hv;
     }

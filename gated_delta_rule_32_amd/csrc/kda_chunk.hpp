@@ -121,4 +121,19 @@ __device__ __forceinline__ void set_prio_by_remaining(int left, int total) {
     }
 }
 
+// XCD-aware order of the work items: the hardware hands blocks to the 8 XCDs
+// round robin (block b to XCD b mod 8), so the G value heads of a q/k head,
+// adjacent in the task list, go to blocks 8 apart (one XCD) and read that
+// head's q and k rows through one L2.  Each window of 8G blocks holds the same
+// items as before (the list's longest-first order at that granularity); a
+// trailing partial window keeps its order.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_order(int b, int n, int G) {
+    const int win = 8 * G;
+    if (G > 1 && b < n / win * win) {
+        const int x = b & 7, y = b >> 3;
+        return G * (8 * (y / G) + x) + y % G;
+    }
+    return b;
+}
+
 }  // namespace kda

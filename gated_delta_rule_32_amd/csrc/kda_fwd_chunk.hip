@@ -136,6 +136,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
     if constexpr (kSegTask) {
         // item = segment index * Hv + h; the segment list holds (n, j) pairs
         int64_t item = blockIdx.x;
+        if constexpr (kRebuild) item = xcd_order((int)item, (int)(gridDim.x), a.G);  // items = segments * Hv
         if constexpr (kSegPQ) {
             segQ = item >= a.seg_items;
             if (segQ) item -= a.seg_items;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(FC_THREADS, 3) void fwd_chunk_kernel(FwdArgs a) {
         n = a.plan.task[2 * sidx];
         seg = a.plan.task[2 * sidx + 1];
     } else {
-        const int code = a.plan.task[blockIdx.x];
+        const int code = a.plan.task[xcd_order(blockIdx.x, a.num_tasks, a.G)];
         n = code / a.Hv;
         h = code - n * a.Hv;
     }
