@@ -472,8 +472,9 @@ struct RecLayout {
 // Pair records (the start state of even chunks only) when the adjoint has
 // tasks enough to hide forming the odd chunks' states: measured with 768
 // tasks (8 x 1024 tokens, 96 heads) the backward is 2.7% faster with them
-// (the rebuild writes 30% fewer bytes), with 128 tasks (4 x 4096 tokens, 32
-// value heads), where each task runs at the latency of its chain, 3.5% slower.
+// (the rebuild writes 30% fewer bytes), 3.6% with 512 (64 heads), 1.1% with
+// 384, the same with 320; with 128 tasks (4 x 4096 tokens, 32 value heads),
+// where each task runs at the latency of its chain, 3.5% slower.
 // (The segment-parallel route, for few tasks, keeps a start state per chunk.)
 constexpr int64_t kPairMinTasks = 256;
 bool rec_pairs(const Prob& p) { return p.num_tasks > kPairMinTasks && p.route != 3; }
